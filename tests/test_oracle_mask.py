@@ -1,0 +1,151 @@
+"""Pins of the oracle's mask and tile index (CPU only).
+
+* the hand-derived worked example in tests/golden/mask_example.txt;
+* brute force over every separator pattern of short sequences (a per-element
+  loop, independent of the oracle's vectorised form);
+* reductions: n >= S or all-separator sequences give the causal mask; no
+  separators give sink + sliding window (built with np.tril/np.triu);
+* closed forms: per-row visible count, anchor count, anchors below a tile.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import sepmask
+
+
+def _ints(s):
+    return [int(x) for x in s.split()]
+
+
+def test_golden_mask_example(golden):
+    g = golden("mask_example.txt")
+    S, a, n = int(g["S"]), int(g["a"]), int(g["n"])
+    tq, tk = int(g["tq"]), int(g["tk"])
+    seps = _ints(g["separators"])
+    sep_ids = [1000 + i for i in range(3)]
+    tok = np.full(S, 7, dtype=np.int64)
+    for p in seps:
+        tok[p] = sep_ids[p % 3]
+    M = sepmask.sep_mask(tok, sep_ids, a, n)
+    for i in range(S):
+        row = g[f"row{i}"]
+        assert "".join("1" if x else "." for x in M[i]) == row, i
+    assert list(M.sum(1)) == _ints(g["nnz"])
+    idx = sepmask.build_index(tok, sep_ids, a, n, tq=tq, tk=tk)
+    assert list(idx["is_sep"]) == _ints(g["is_sep"])
+    assert list(idx["sep_prefix"]) == _ints(g["sep_prefix"])
+    assert list(idx["anchor_pos"]) == _ints(g["anchor_pos"])
+    assert idx["anchor_count"] == int(g["anchor_count"])
+    for qi in range(idx["qtile"].shape[0]):
+        assert list(idx["qtile"][qi]) == _ints(g[f"qtile{qi}"]), qi
+        assert list(idx["tile_class"][qi]) == _ints(g[f"class{qi}"]), qi
+
+
+def _brute_mask(sep, a, n):
+    S = len(sep)
+    M = np.zeros((S, S), dtype=bool)
+    for i in range(S):
+        for j in range(S):
+            if j > i:
+                continue
+            if j < a or sep[j] or i - j < n:
+                M[i, j] = True
+    return M
+
+
+def _tok_from_flags(flags, sep_ids=(11, 12)):
+    tok = np.array([sep_ids[k % 2] if f else 3 + k for k, f in enumerate(flags)])
+    return tok, list(sep_ids)
+
+
+def _check_index_against_mask(tok, sep_ids, a, n, tq, tk):
+    S = len(tok)
+    sep = np.isin(tok, sep_ids)
+    M = _brute_mask(sep, a, n)
+    assert np.array_equal(sepmask.sep_mask(tok, sep_ids, a, n), M)
+    idx = sepmask.build_index(tok, sep_ids, a, n, tq=tq, tk=tk)
+    anchors = [int(p) for p in idx["anchor_pos"] if p >= 0]
+    # closed form of the anchor count and of every row's visible count
+    assert idx["anchor_count"] == min(a, S) + int(sep[a:].sum())
+    sp = idx["sep_prefix"]
+    for i in range(S):
+        lo_i = max(0, i - n + 1)
+        assert M[i].sum() == (i - lo_i + 1) + min(a, lo_i) + sp[lo_i]
+    QT = -(-S // tq)
+    KT = -(-S // tk)
+    for qi in range(QT):
+        lo, n_anchor, kb, ke, n_kept, rows = [int(x) for x in idx["qtile"][qi]]
+        q0, q1 = tq * qi, min(tq * qi + tq - 1, S - 1)
+        assert n_anchor == min(a, lo) + sp[lo]
+        # partition identity: visible keys of every row = anchors below lo
+        # (disjoint) + the masked band [lo, i]
+        for i in range(q0, q1 + 1):
+            vis = set(np.nonzero(M[i])[0].tolist())
+            below = anchors[:n_anchor]
+            assert all(p < lo for p in below)
+            band = {j for j in range(lo, i + 1) if M[i, j]}
+            assert vis == set(below) | band
+            assert not (set(below) & band)
+            # the band lies inside key tiles kt_begin..kt_end
+            assert all(kb * tk <= j <= ke * tk + tk - 1 for j in band)
+        for kj in range(KT):
+            blk = M[q0:q1 + 1, tk * kj:min(tk * kj + tk, S)]
+            want = 0 if blk.sum() == 0 else (2 if blk.all() else 1)
+            assert idx["tile_class"][qi, kj] == want
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 8])
+def test_brute_force_all_patterns(S):
+    for flags in itertools.product([False, True], repeat=S):
+        tok, sep_ids = _tok_from_flags(flags)
+        for a in range(0, 4):
+            for n in range(1, S + 1):
+                _check_index_against_mask(tok, sep_ids, a, n, tq=4, tk=2)
+
+
+def test_brute_force_random_longer():
+    r = np.random.default_rng(123)
+    for _ in range(60):
+        S = int(r.integers(9, 40))
+        flags = r.random(S) < r.random()
+        tok, sep_ids = _tok_from_flags(flags)
+        a = int(r.integers(0, 6))
+        n = int(r.integers(1, S + 2))
+        tq = int(r.choice([2, 4, 8]))
+        tk = int(r.choice([1, 2, 4]))
+        _check_index_against_mask(tok, sep_ids, a, n, tq, tk)
+
+
+def test_dense_reduction():
+    """n >= S, or every token a separator: the mask is plain causal."""
+    S = 37
+    causal = np.tril(np.ones((S, S), dtype=bool))
+    tok = np.arange(S) + 100
+    assert np.array_equal(sepmask.sep_mask(tok, [5], 2, S), causal)
+    assert np.array_equal(sepmask.sep_mask(tok, [5], 0, S + 10), causal)
+    allsep = np.full(S, 5)
+    assert np.array_equal(sepmask.sep_mask(allsep, [5], 0, 1), causal)
+
+
+def test_streaming_reduction():
+    """No separators: sink tokens + sliding window (StreamingLLM's pattern),
+    built here from triangular matrices."""
+    S = 50
+    tok = np.arange(S) + 100
+    for a, n in [(0, 1), (4, 8), (3, 17), (0, 50)]:
+        ones = np.ones((S, S), dtype=bool)
+        band = np.tril(ones) & np.triu(ones, -(n - 1))
+        sink = np.tril(ones) & (np.arange(S)[None, :] < a)
+        assert np.array_equal(sepmask.sep_mask(tok, [7], a, n), band | sink)
+
+
+def test_kept_entries_counts_tiles():
+    tok = np.arange(300) % 13
+    idx = sepmask.build_index(tok, [0, 5], 4, 64)
+    E = sepmask.kept_entries(idx["qtile"])
+    nnz = sepmask.row_nnz(np.isin(tok, [0, 5]), 4, 64).sum()
+    assert nnz <= E  # kept tiles cover every visible entry
+    assert E == sum(int(r[5]) * 64 * int(r[4]) for r in idx["qtile"])
