@@ -1,0 +1,55 @@
+// Shared device-side helpers of libsepattn (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sepattn.h"
+
+namespace sepattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kQTile = SEPATTN_QTILE;
+constexpr int kKTile = SEPATTN_KTILE;
+constexpr int kQF = SEPATTN_QTILE_FIELDS;
+
+// Separator id set passed by value in kernel arguments.
+struct SepSet {
+  int n;
+  int32_t ids[SEPATTN_MAX_SEP_IDS];
+};
+
+__device__ __forceinline__ bool is_separator(const SepSet& s, int32_t tok) {
+  bool hit = false;
+  for (int i = 0; i < s.n; ++i) hit |= (s.ids[i] == tok);
+  return hit;
+}
+
+// bf16 <-> f32 (round to nearest even), bit-level so the rounding is explicit.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// two floats -> packed pair of bf16 (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Swap with the lane 32 apart (the other half of the wave).
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+}  // namespace sepattn

@@ -1,0 +1,257 @@
+// Forward of SepLLM separator-sparse attention: block-sparse flash attention
+// over the kept tiles of each 128-row query tile -- ceil(n_anchor/64) tiles of
+// gathered anchors (initial tokens and separators below the window, visible to
+// every row of the tile, so unmasked) and the key tiles kt_begin..kt_end of
+// the local band (masked element-wise).  Online softmax in the base-2 domain,
+// fp32 accumulation, P rounded to the input type for the second product.
+//
+// Mask: SepLLM summary on atlas.scime.ai, "Approach".  Output O = M(A, V, M_b)
+// read as softmax renormalised over the kept keys ("How SepLLM Reorchestrates
+// the Language Model for Speed and Efficiency", "SepLLM's Architecture").
+#include "internal.hpp"
+#include "tile.hpp"
+
+namespace sepattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const uint8_t* is_sep;
+  const int32_t* anchor_pos;
+  const int32_t* qtile;
+  int B, Hq, Hkv, S, a, n, QT;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+constexpr int kFwdThreads = 256;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kFwdThreads) fwd_kernel(FwdArgs p) {
+  typedef Traits<T> Tr;
+  typedef TileGeom<T, D> G;
+  typedef typename Tr::frag frag;
+  constexpr int EPL = Tr::EPL;
+  constexpr int KSTEP = Tr::KSTEP;
+  constexpr int NQF = D / KSTEP;      // Q fragments per lane
+  constexpr int NDB = D / 32;         // 32-row blocks of O^T
+  constexpr int NPS = kKTile / KSTEP; // MFMA steps of P V per tile
+
+  __shared__ __attribute__((aligned(16))) T Ks[G::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) T Vt[G::V_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hh = lane >> 5;
+  const int qc = lane & 31;
+
+  // heaviest query tiles (most anchors) are dispatched first
+  const int qi = p.QT - 1 - (int)blockIdx.y;
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / (p.Hq / p.Hkv);
+
+  const int32_t* qt = p.qtile + ((size_t)b * p.QT + qi) * kQF;
+  const int lo = qt[0], n_anchor = qt[1], kb = qt[2], ke = qt[3], q0 = qt[6];
+  const int n_at = (n_anchor + kKTile - 1) / kKTile;
+  const int n_tiles = n_at + ke - kb + 1;
+
+  const int iq = q0 + 32 * w + qc;  // this lane's query row
+  const bool q_ok = iq < p.S;
+  const T* Qg = (const T*)p.q + (((size_t)b * p.Hq + h) * p.S) * D;
+  const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
+  const T* Vg = (const T*)p.v + (((size_t)b * p.Hkv + g) * p.S) * D;
+  const int32_t* anc = p.anchor_pos + (size_t)b * p.S;
+  const uint8_t* sepf = p.is_sep + (size_t)b * p.S;
+
+  frag qf[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) {
+    if (q_ok) qf[c] = *(const frag*)(Qg + (size_t)iq * D + c * KSTEP + EPL * hh);
+    else qf[c] = frag{};
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY;  // running max (base-2 domain), shared by the lane pair
+  float l = 0.f;        // this lane's part of the running sum
+
+  const int wrow0 = q0 + 32 * w;
+  const int wrow1 = min(wrow0 + 31, p.S - 1);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool anchor_tile = t < n_at;
+    const int kt = kb + (t - n_at);
+    RowSrc src;
+    if (anchor_tile) {
+      src.anchor = anc;
+      src.base = t * kKTile;
+      src.limit = n_anchor;
+    } else {
+      src.anchor = nullptr;
+      src.base = kt * kKTile;
+      src.limit = p.S;
+    }
+    __syncthreads();
+    load_k_tile<T, D, kFwdThreads>(Ks, Kg, src, tid);
+    load_vt_tile<T, D, kFwdThreads>(Vt, Vg, src, tid);
+    uint64_t sepbits = 0;
+    if (!anchor_tile) {
+      const int j = kt * kKTile + lane;
+      sepbits = __ballot(j < p.S && sepf[j] != 0);
+    }
+    __syncthreads();
+
+    // S^T = K Q^T for the two 32-key halves of the tile
+    f32x16 sacc[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      f32x16 acc = f32x16{};
+      const T* krow = Ks + (32 * k2 + qc) * G::KSTR + EPL * hh;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(*(const frag*)(krow + c * KSTEP), qf[c], acc);
+      sacc[k2] = acc;
+    }
+
+    // scale and mask
+    bool full;
+    if (anchor_tile) {
+      full = (t + 1) * kKTile <= n_anchor;
+    } else {
+      const int c0 = kt * kKTile;
+      full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = sacc[k2][i] * p.scale_log2;
+        if (!full) {
+          const int r = 32 * k2 + acc_row(i, hh);
+          bool vis;
+          if (anchor_tile) {
+            vis = t * kKTile + r < n_anchor;
+          } else {
+            const int j = kt * kKTile + r;
+            vis = j < p.S && j >= lo && j <= iq &&
+                  (j < p.a || ((sepbits >> r) & 1ull) || iq - j < p.n);
+          }
+          s = vis ? s : -INFINITY;
+        }
+        sacc[k2][i] = s;
+      }
+    }
+
+    // online softmax update
+    float mloc = m;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[k2][i]);
+    const float m_new = fmaxf(mloc, xor32(mloc));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(sacc[k2][i] - m_use);
+        sacc[k2][i] = pv;
+        psum += pv;
+      }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int s = 0; s < NPS; ++s) {
+      const int k2 = s / (32 / KSTEP);
+      const int sl = s % (32 / KSTEP);
+      frag pf;
+      if constexpr (EPL == 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)sacc[k2][sl * 8 + j];
+      } else {
+        pf = sacc[k2][sl];
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const frag vf = *(const frag*)(Vt + (32 * db + qc) * G::VSTR + 32 * k2 + sl * 2 * EPL + hh * EPL);
+        oacc[db] = Tr::mfma(vf, pf, oacc[db]);
+      }
+    }
+  }
+
+  // normalise and store
+  const float l_tot = l + xor32(l);
+  const float inv = 1.f / l_tot;
+  if (q_ok) {
+    T* Og = (T*)p.o + (((size_t)b * p.Hq + h) * p.S + iq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * db + 8 * r4 + 4 * hh;
+        if constexpr (EPL == 8) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+          pk[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+          *(u32x2*)(Og + d0) = pk;
+        } else {
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = oacc[db][4 * r4 + e] * inv;
+          *(f32x4*)(Og + d0) = ov;
+        }
+      }
+    }
+    if (hh == 0) {
+      // natural-log normaliser of the scaled scores
+      p.lse[((size_t)b * p.Hq + h) * p.S + iq] = (m + fast_log2(l_tot)) * 0.69314718055994530942f;
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  dim3 grid(a.B * a.Hq, a.QT);
+  hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kFwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const AttnShape& sh,
+                      const sepattn_index& idx, void* o, float* lse, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.is_sep = idx.is_sep;
+  a.anchor_pos = idx.anchor_pos;
+  a.qtile = idx.qtile;
+  a.B = sh.B;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.S = sh.S;
+  a.a = idx.a;
+  a.n = idx.n;
+  a.QT = (sh.S + kQTile - 1) / kQTile;
+  a.scale_log2 = sh.scale * 1.4426950408889634f;
+  if (sh.dtype == SEPATTN_BF16) {
+    if (sh.d == 64) return launch_fwd_t<__bf16, 64>(a, stream);
+    return launch_fwd_t<__bf16, 128>(a, stream);
+  }
+  if (sh.d == 64) return launch_fwd_t<float, 64>(a, stream);
+  return launch_fwd_t<float, 128>(a, stream);
+}
+
+}  // namespace sepattn

@@ -1,0 +1,166 @@
+// Index builder: separator flags, separator prefix counts, the anchor list
+// (initial tokens then separators, a stream compaction) and the per-tile
+// schedule / block-sparsity classes of the SepLLM mask.
+//
+// The mask (SepLLM summary on atlas.scime.ai, "Approach"): query i sees key j
+// iff j <= i and (j < a or tok[j] is a separator or i - j < n).
+#include "internal.hpp"
+
+namespace sepattn {
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 8;  // consecutive tokens per thread per chunk
+
+// One workgroup per sequence.  Chunks of kScanThreads * kScanItems tokens are
+// scanned in order with a running carry, so the result is deterministic.
+__global__ void __launch_bounds__(kScanThreads)
+index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep,
+                  uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_prefix,
+                  int32_t* __restrict__ anchor_pos, int32_t* __restrict__ anchor_count) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wid = t / kWave;
+  constexpr int kWaves = kScanThreads / kWave;
+  __shared__ int wave_sum[kWaves];
+  __shared__ int carry_sh;
+
+  const int32_t* tk = tok + (size_t)b * S;
+  uint8_t* fl = is_sep + (size_t)b * S;
+  int32_t* pre = sep_prefix + (size_t)b * (S + 1);
+  int32_t* anc = anchor_pos + (size_t)b * S;
+  const int n_init = a < S ? a : S;
+
+  if (t == 0) carry_sh = 0;
+  __syncthreads();
+
+  for (int base = 0; base < S; base += kScanThreads * kScanItems) {
+    const int j0 = base + t * kScanItems;
+    int f[kScanItems];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kScanItems; ++e) {
+      const int j = j0 + e;
+      int s = 0;
+      if (j < S) {
+        s = is_separator(sep, tk[j]) ? 1 : 0;
+        fl[j] = (uint8_t)s;
+      }
+      f[e] = (j < S && j >= a) ? s : 0;  // separators counted from position a on
+      cnt += f[e];
+    }
+    // inclusive scan of cnt across the wave
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) wave_sum[wid] = incl;
+    __syncthreads();
+    int wave_off = 0;
+    int chunk_total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int ws = wave_sum[w];
+      wave_off += (w < wid) ? ws : 0;
+      chunk_total += ws;
+    }
+    const int carry = carry_sh;
+    int run = carry + wave_off + incl - cnt;  // exclusive prefix at j0
+#pragma unroll
+    for (int e = 0; e < kScanItems; ++e) {
+      const int j = j0 + e;
+      if (j < S) {
+        pre[j] = run;
+        if (j < n_init) anc[j] = j;
+        else if (f[e]) anc[n_init + run] = j;
+      }
+      run += f[e];
+    }
+    __syncthreads();
+    if (t == 0) carry_sh = carry + chunk_total;
+    __syncthreads();
+  }
+  const int total = carry_sh;
+  if (t == 0) {
+    pre[S] = total;
+    anchor_count[b] = n_init + total;
+  }
+  // pad the anchor list with -1
+  for (int j = n_init + total + t; j < S; j += kScanThreads) anc[j] = -1;
+}
+
+// Visible entries of the mask in row i over key columns [c0, c1] (c1 < S).
+__device__ __forceinline__ int row_count(int i, int c0, int c1, int a, int n,
+                                         const int32_t* __restrict__ pre) {
+  const int hi = c1 < i ? c1 : i;
+  if (hi < c0) return 0;
+  const int w0 = (i - n + 1) > c0 ? (i - n + 1) : c0;
+  int cnt = hi >= w0 ? hi - w0 + 1 : 0;  // window part
+  const int e = hi < (i - n) ? hi : (i - n);  // last key outside the window
+  if (e >= c0) {
+    const int ie = e < a - 1 ? e : a - 1;
+    if (ie >= c0) cnt += ie - c0 + 1;  // initial tokens
+    const int s0 = c0 > a ? c0 : a;
+    if (e >= s0) cnt += pre[e + 1] - pre[s0];  // separators
+  }
+  return cnt;
+}
+
+// Grid (QT, B): per query tile, its schedule fields and the class of every
+// 128 x 64 tile in its row of the grid.
+__global__ void __launch_bounds__(256)
+index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
+                   int32_t* __restrict__ qtile, uint8_t* __restrict__ tile_class) {
+  const int qi = blockIdx.x;
+  const int b = blockIdx.y;
+  const int QT = gridDim.x;
+  const int KT = (S + kKTile - 1) / kKTile;
+  const int32_t* pre = sep_prefix + (size_t)b * (S + 1);
+  const int q0 = qi * kQTile;
+  const int q1 = min(q0 + kQTile - 1, S - 1);
+  if (threadIdx.x == 0) {
+    const int lo = max(0, q0 - n + 1);
+    const int n_anchor = min(a, lo) + pre[lo];
+    const int kb = lo / kKTile;
+    const int ke = q1 / kKTile;
+    int32_t* f = qtile + ((size_t)b * QT + qi) * kQF;
+    f[0] = lo;
+    f[1] = n_anchor;
+    f[2] = kb;
+    f[3] = ke;
+    f[4] = (n_anchor + kKTile - 1) / kKTile + ke - kb + 1;
+    f[5] = q1 - q0 + 1;
+    f[6] = q0;
+    f[7] = 0;
+  }
+  uint8_t* cls = tile_class + ((size_t)b * QT + qi) * KT;
+  for (int kj = threadIdx.x; kj < KT; kj += blockDim.x) {
+    const int c0 = kj * kKTile;
+    const int c1 = min(c0 + kKTile - 1, S - 1);
+    uint8_t c;
+    if (c0 > q1) {
+      c = 0;  // entirely above the diagonal
+    } else {
+      int total = 0;
+      for (int i = q0; i <= q1; ++i) total += row_count(i, c0, c1, a, n, pre);
+      const int full = (q1 - q0 + 1) * (c1 - c0 + 1);
+      c = total == 0 ? 0 : (total == full ? 2 : 1);
+    }
+    cls[kj] = c;
+  }
+}
+
+hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int a, int n,
+                              const sepattn_index& idx, hipStream_t stream) {
+  hipLaunchKernelGGL(index_scan_kernel, dim3(B), dim3(kScanThreads), 0, stream, tok, S, a, sep,
+                     idx.is_sep, idx.sep_prefix, idx.anchor_pos, idx.anchor_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int QT = (S + kQTile - 1) / kQTile;
+  hipLaunchKernelGGL(index_tiles_kernel, dim3(QT, B), dim3(256), 0, stream, S, a, n,
+                     idx.sep_prefix, idx.qtile, idx.tile_class);
+  return hipGetLastError();
+}
+
+}  // namespace sepattn

@@ -1,0 +1,39 @@
+// Internal launcher declarations of libsepattn (host side of each .hip file).
+#pragma once
+
+#include "common.hpp"
+
+namespace sepattn {
+
+// Largest SepCache capacity c the update kernel plans in LDS.
+constexpr int kMaxCacheCapacity = 8192;
+// Largest kv-head count of a SepCache (one slot over all heads, K and V, must
+// fit the update kernel's move chunk: 2 * Hkv * d * 2 bytes <= 1024 * 8 * 16).
+constexpr int kMaxCacheHeads = 128;
+// Largest number of query heads per kv head in decode.
+constexpr int kMaxDecodeGroup = 8;
+
+hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int a, int n,
+                              const sepattn_index& idx, hipStream_t stream);
+
+struct AttnShape {
+  int B, Hq, Hkv, S, d, dtype;
+  float scale;
+};
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const AttnShape& sh,
+                      const sepattn_index& idx, void* o, float* lse, hipStream_t stream);
+
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, const AttnShape& sh, const sepattn_index& idx, void* dq,
+                      void* dk, void* dv, void* ws, hipStream_t stream);
+
+hipError_t launch_cache_init(const sepcache& c, hipStream_t stream);
+hipError_t launch_cache_update(const sepcache& c, const void* k_new, const void* v_new,
+                               const int32_t* tok_new, const SepSet& sep, hipStream_t stream);
+size_t decode_workspace_bytes(const sepcache& c, int Hq);
+hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* rope_cos,
+                         const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream);
+
+}  // namespace sepattn

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every symbol include/sepattn.h declares,
+and rejects bad arguments on the host before anything is launched (CPU only:
+no call here reaches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch  # noqa: F401  (loads torch's HIP runtime before the library)
+
+import sparse_attention_sepattn_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sepattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sep\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sa.load_library()
+    names = declared_functions()
+    assert set(names) == set(sa.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror_and_sizes():
+    L = sa.load_library()
+    for st in range(6):
+        assert L.sepattn_strerror(st)
+    assert L.sepattn_index_bytes(0, 10) == 0
+    n = L.sepattn_index_bytes(2, 1000)
+    assert n >= 2 * 1000 * (1 + 4 + 4) and n % 256 == 0
+
+
+def test_index_bind_carves_buffer_without_touching_it():
+    L = sa.load_library()
+    B, S = 3, 300
+    n = L.sepattn_index_bytes(B, S)
+    st = sa._Index()
+    base = 1 << 40  # never dereferenced: bind only computes addresses
+    assert L.sepattn_index_bind(ctypes.c_void_p(base), n, B, S, ctypes.byref(st)) == 0
+    ptrs = [st.is_sep, st.sep_prefix, st.anchor_pos, st.anchor_count, st.qtile, st.tile_class]
+    assert ptrs == sorted(ptrs) and all(p % 256 == 0 for p in ptrs)
+    assert st.tile_class + B * 3 * 5 <= base + n
+    assert L.sepattn_index_bind(ctypes.c_void_p(base), n - 1, B, S, ctypes.byref(st)) == 4
+    assert L.sepattn_index_bind(ctypes.c_void_p(base + 8), n, B, S, ctypes.byref(st)) == 1
+
+
+def test_argument_errors_are_host_side():
+    L = sa.load_library()
+    fake = ctypes.c_void_p(1 << 40)
+    st = sa._Index()
+    L.sepattn_index_bind(fake, L.sepattn_index_bytes(1, 64), 1, 64, ctypes.byref(st))
+    st.n = 4
+    z = ctypes.c_void_p(0)
+    # unsupported head dim, bad GQA ratio, null pointers
+    assert L.sepattn_fwd(fake, fake, fake, 1, 2, 1, 64, 96, 1, 0.1, ctypes.byref(st), fake, fake, z) == 2
+    assert L.sepattn_fwd(fake, fake, fake, 1, 3, 2, 64, 64, 1, 0.1, ctypes.byref(st), fake, fake, z) == 1
+    assert L.sepattn_fwd(z, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st), fake, fake, z) == 1
+    # index bound for another shape
+    assert L.sepattn_fwd(fake, fake, fake, 1, 2, 1, 128, 64, 1, 0.1, ctypes.byref(st), fake, fake, z) == 1
+    # build_index: n < 1, a < 0, too many separator ids
+    ids = (ctypes.c_int32 * 65)(*range(65))
+    assert L.sepattn_build_index(fake, 1, 64, ids, 3, 4, 0, ctypes.byref(st), z) == 1
+    assert L.sepattn_build_index(fake, 1, 64, ids, 3, -1, 4, ctypes.byref(st), z) == 1
+    assert L.sepattn_build_index(fake, 1, 64, ids, 65, 4, 4, ctypes.byref(st), z) == 1
+    # bwd workspace too small
+    need = L.sepattn_bwd_workspace(1, 2, 1, 64, 64, 1)
+    assert need > 0
+    assert L.sepattn_bwd(fake, fake, fake, fake, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st),
+                         fake, fake, fake, fake, need - 1, z) == 4
+
+
+def test_cache_capacity_errors():
+    L = sa.load_library()
+    fake = 1 << 40
+    c = sa._Cache(2, 8, 128, 324, 4, 64, 256, fake, fake, fake, fake, fake)
+    z = ctypes.c_void_p(0)
+    assert L.sepcache_init(ctypes.byref(c), z) == 3          # c <= a + s + w
+    c.c, c.w = 800, 0
+    assert L.sepcache_init(ctypes.byref(c), z) == 3          # w < 1
+    c.w, c.d = 256, 96
+    assert L.sepcache_init(ctypes.byref(c), z) == 2          # head dim
+    c.d = 128
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 32) > 0
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 30) == 0   # Hq % Hkv
+    fp = ctypes.c_void_p(fake)
+    assert L.sepcache_decode(ctypes.byref(c), fp, 96, fp, fp, 0.1, fp, fp, 1 << 30, z) == 2  # group of 12
+
+
+def test_rope_table_host_matches_double_precision():
+    c, d, theta = 800, 128, 500000.0
+    cos, sin = sa.rope_table(theta, c, d)
+    p = np.arange(c)[:, None].astype(np.float64)
+    f = theta ** (-2.0 * np.arange(d // 2) / d)
+    assert np.array_equal(cos, np.cos(p * f).astype(np.float32))
+    assert np.array_equal(sin, np.sin(p * f).astype(np.float32))
