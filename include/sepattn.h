@@ -153,6 +153,17 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* sepattn_bwd with per-kernel timing: `events` is a HOST array of n_events
+ * >= 5 hipEvent_t (created by the caller, passed as void*).  events[0] is
+ * recorded on `stream` before the first kernel and events[i] after the i-th
+ * of the four kernels: (1) row sums D = rowsum(dO * O), (2) key-major dK/dV
+ * over gathered anchor tiles, (3) key-major dK/dV over band tiles, (4)
+ * query-major dQ.  Results are identical to sepattn_bwd. */
+int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
+                         const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events, int n_events);
+
 /* ------------------------------------------------------------------------ */
 /* SepCache (streaming)                                                      */
 /* ------------------------------------------------------------------------ */

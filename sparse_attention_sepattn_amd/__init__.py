@@ -55,7 +55,8 @@ class _Cache(ctypes.Structure):
 
 
 EXPORTS = ["sepattn_strerror", "sepattn_index_bytes", "sepattn_index_bind", "sepattn_build_index",
-           "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepcache_init", "sepcache_update",
+           "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepattn_bwd_profiled",
+           "sepcache_init", "sepcache_update",
            "sepcache_decode_workspace", "sepcache_decode", "sepattn_rope_table_host"]
 
 
@@ -86,6 +87,9 @@ def load_library(path=None):
     L.sepattn_bwd.restype = i32
     L.sepattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                               ctypes.POINTER(_Index), vp, vp, vp, vp, sz, vp]
+    L.sepattn_bwd_profiled.restype = i32
+    L.sepattn_bwd_profiled.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                       ctypes.POINTER(_Index), vp, vp, vp, vp, sz, vp, vp, i32]
     L.sepcache_init.restype = i32
     L.sepcache_init.argtypes = [ctypes.POINTER(_Cache), vp]
     L.sepcache_update.restype = i32
@@ -212,8 +216,10 @@ def bwd_workspace_bytes(B, Hq, Hkv, S, d, dtype=torch.bfloat16):
     return load_library().sepattn_bwd_workspace(B, Hq, Hkv, S, d, code)
 
 
-def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=None):
-    """Backward: gradients of sum(o * dout) -> (dq, dk, dv)."""
+def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=None, events=None):
+    """Backward: gradients of sum(o * dout) -> (dq, dk, dv).  ``events``: an
+    optional sequence of 5 hipEvent_t handles (ints) recorded around the four
+    kernels (see sepattn_bwd_profiled)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     for t, name in ((q, "q"), (o, "o"), (dout, "dout")):
@@ -230,9 +236,13 @@ def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=
     nbytes = L.sepattn_bwd_workspace(B, Hq, Hkv, S, d, _dtype_code(q))
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    _check(L.sepattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), B, Hq, Hkv, S, d,
-                         _dtype_code(q), float(scale), ctypes.byref(index.st), _ptr(dq), _ptr(dk),
-                         _ptr(dv), _ptr(ws), ws.numel(), _stream()), "bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), B, Hq, Hkv, S, d, _dtype_code(q),
+            float(scale), ctypes.byref(index.st), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream())
+    if events is None:
+        _check(L.sepattn_bwd(*args), "bwd")
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(L.sepattn_bwd_profiled(*args, arr, len(events)), "bwd_profiled")
     return dq, dk, dv
 
 

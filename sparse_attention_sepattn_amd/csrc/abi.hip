@@ -127,10 +127,10 @@ size_t sepattn_bwd_workspace(int B, int Hq, int Hkv, int S, int d, int dtype) {
   return bwd_workspace_bytes(B, Hq, Hkv, S, d);
 }
 
-int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
-                const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                void* stream) {
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
+                      const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                      void* stream, hipEvent_t* ev) {
   int st = check_attn(B, Hq, Hkv, S, d, dtype, scale);
   if (st != SEPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !index_ok(idx, B, S))
@@ -138,7 +138,26 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
   if (!ws || ((uintptr_t)ws & 255) != 0) return SEPATTN_EINVAL;
   if (ws_bytes < bwd_workspace_bytes(B, Hq, Hkv, S, d)) return SEPATTN_EWORKSPACE;
   AttnShape sh{B, Hq, Hkv, S, d, dtype, scale};
-  return to_status(launch_bwd(q, k, v, o, lse, dout, sh, *idx, dq, dk, dv, ws, (hipStream_t)stream));
+  return to_status(launch_bwd(q, k, v, o, lse, dout, sh, *idx, dq, dk, dv, ws, (hipStream_t)stream, ev));
+}
+
+int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
+                const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, B, Hq, Hkv, S, d, dtype, scale, idx, dq, dk, dv, ws, ws_bytes,
+                    stream, nullptr);
+}
+
+int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
+                         const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events, int n_events) {
+  if (!events || n_events < kBwdLaunches + 1) return SEPATTN_EINVAL;
+  for (int i = 0; i <= kBwdLaunches; ++i)
+    if (!events[i]) return SEPATTN_EINVAL;
+  return bwd_common(q, k, v, o, lse, dout, B, Hq, Hkv, S, d, dtype, scale, idx, dq, dk, dv, ws, ws_bytes,
+                    stream, (hipEvent_t*)events);
 }
 
 int sepcache_init(const sepcache* cache, void* stream) {
@@ -170,7 +189,8 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
   if (st != SEPATTN_OK) return st;
   if (!q || !rope_cos || !rope_sin || !o || Hq < 1 || Hq % cache->Hkv != 0 || !isfinite(scale))
     return SEPATTN_EINVAL;
-  if (Hq / cache->Hkv > kMaxDecodeGroup) return SEPATTN_EUNSUPPORTED;
+  const int G = Hq / cache->Hkv;
+  if (G > kMaxDecodeGroup || (G & (G - 1)) != 0) return SEPATTN_EUNSUPPORTED;
   if (!ws || ((uintptr_t)ws & 255) != 0) return SEPATTN_EINVAL;
   if (ws_bytes < decode_workspace_bytes(*cache, Hq)) return SEPATTN_EWORKSPACE;
   return to_status(launch_decode(*cache, q, Hq, rope_cos, rope_sin, scale, o, ws, (hipStream_t)stream));

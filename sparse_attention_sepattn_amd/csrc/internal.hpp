@@ -25,9 +25,12 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const AttnSha
                       const sepattn_index& idx, void* o, float* lse, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
+// `ev` (nullable): kBwdLaunches + 1 events recorded before the first launch
+// and after each launch, for per-kernel timing.
+constexpr int kBwdLaunches = 4;
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, const AttnShape& sh, const sepattn_index& idx, void* dq,
-                      void* dk, void* dv, void* ws, hipStream_t stream);
+                      void* dk, void* dv, void* ws, hipStream_t stream, hipEvent_t* ev);
 
 hipError_t launch_cache_init(const sepcache& c, hipStream_t stream);
 hipError_t launch_cache_update(const sepcache& c, const void* k_new, const void* v_new,
