@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Throughput of the SepLLM separator-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One JSON line on stdout.  The main workload is the Pythia-160m-shaped
+training step of the attention: B=8, 12 heads, S=2048, d=64, bf16, separator
+probability 0.08 over 9 ids, a=4 initial tokens, window n=64.  One step is
+the whole prefill/training path over one batch: index build (separator flags,
+anchors, tile schedule), forward, backward.  Inputs are seeded synthetic data
+resident in HBM before the timed region.
+
+value = kept-tile TFLOP/s of forward+backward, counted on the canonical
+schedule the index defines (E = sum over query tiles of rows * 64 * kept
+tiles; forward 4*d*E, backward 10*d*E, over batch x heads), divided by the
+measured step time (index build included).  The useful-entry count
+(visible mask entries) and the tile efficiency are reported beside it.
+
+roofline: the kernel with the largest average duration, its algorithmic
+FLOPs on the same schedule (2 GEMMs per kept tile for the forward, 3 for the
+query-major dQ, 4 for the key-major dK/dV) over its duration measured with
+HIP events on the launch stream during the timed steps, against the bf16
+dense MFMA peak.
+
+decode: the streaming SepCache workload (B=64, 32 q / 8 kv heads, d=128,
+c=800 = 4 initial + 64 separator slots + a 256-token window, RoPE theta
+500000 by slot), 4096 steps of update + decode; HBM GB/s of the decode kernel
+over the steady state (steps 1024..4095), counting every cached K/V row read
+once per step per kv head plus the queries.
+
+cpu_baseline: the fp64 CPU oracle (plain numpy, materialised mask) timed on a
+bounded sample of the same workload (the first heads of sequence 0), scaled
+to the same unit.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Events:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch
+    loaded), recorded by the library's profiled entry points."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+            self.made.append(e.value)
+        return out
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def schedule_counts(qtile, sep_prefix, a, n, S, tk=64):
+    """Kept-tile entries (total, anchor part, band part) and visible entries
+    of one sequence, from its index (qtile fields and separator prefix)."""
+    qt = qtile.astype(np.int64)
+    rows, n_anchor, kb, ke, n_kept = qt[:, 5], qt[:, 1], qt[:, 2], qt[:, 3], qt[:, 4]
+    E = int((rows * tk * n_kept).sum())
+    Ea = int((rows * tk * ((n_anchor + tk - 1) // tk)).sum())
+    Eb = int((rows * tk * (ke - kb + 1)).sum())
+    i = np.arange(S, dtype=np.int64)
+    lo = np.maximum(0, i - n + 1)
+    nnz = int(((i - lo + 1) + np.minimum(a, lo) + sep_prefix.astype(np.int64)[lo]).sum())
+    return E, Ea, Eb, nnz
+
+
+def traffic_from_profiles(kernel):
+    """HBM bytes per launch from the committed counter summary of `kernel`,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import hashlib
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+        if not rec:
+            return None
+        src = os.path.join(ROOT, "sparse_attention_sepattn_amd", "csrc", rec["source"])
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        if digest != rec["source_sha256"]:
+            return None
+        return rec["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def prefill_leg(args, torch, sa, synth):
+    cfg = synth.CONFIGS["pythia160m"]
+    B, Hq, Hkv, S, d, a, n = (cfg[x] for x in ("B", "Hq", "Hkv", "S", "d", "a", "n"))
+    inp = synth.prefill_inputs(cfg)
+    dev = torch.device("cuda:0")
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = bf(inp["q"]), bf(inp["k"]), bf(inp["v"]), bf(inp["do"])
+    tok = torch.from_numpy(inp["tok"]).to(dev)
+    sep = inp["sep"]
+    scale = float(inp["scale"])
+    idx = sa.Index(B, S, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(sa.bwd_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8, device=dev)
+    ev = Events()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(marks=None):
+        if marks is not None:
+            ev.record(marks[0], stream)
+        sa.build_index(tok, sep, a, n, index=idx)
+        if marks is not None:
+            ev.record(marks[1], stream)
+        sa.fwd(q, k, v, idx, scale, o=o, lse=lse)
+        if marks is not None:
+            ev.record(marks[2], stream)
+        sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws,
+               events=None if marks is None else marks[3:8])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    marks = [ev.new(8) for _ in range(K)]
+    t_start, t_end = ev.new(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.record(t_start, stream)
+    for s in range(K):
+        step(marks[s])
+    ev.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.ms(t_start, t_end)
+    names = ["index", "fwd", "bwd_rowsum", "bwd_dkdv_anchor", "bwd_dkdv_band", "bwd_dq"]
+    seg = {nm: [] for nm in names}
+    for m in marks:
+        seg["index"].append(ev.ms(m[0], m[1]))
+        seg["fwd"].append(ev.ms(m[1], m[2]))
+        seg["bwd_rowsum"].append(ev.ms(m[3], m[4]))
+        seg["bwd_dkdv_anchor"].append(ev.ms(m[4], m[5]))
+        seg["bwd_dkdv_band"].append(ev.ms(m[5], m[6]))
+        seg["bwd_dq"].append(ev.ms(m[6], m[7]))
+    avg = {nm: float(np.mean(x)) for nm, x in seg.items()}
+    ev.close()
+
+    # work on the canonical schedule, from the index the step built
+    qtile = idx.qtile.cpu().numpy()
+    pref = idx.sep_prefix.cpu().numpy()
+    E = Ea = Eb = nnz = 0
+    E_seq0 = None
+    for b in range(B):
+        e, ea, eb, nz = schedule_counts(qtile[b], pref[b], a, n, S)
+        if b == 0:
+            E_seq0 = e
+        E += e * Hq
+        Ea += ea * Hq
+        Eb += eb * Hq
+        nnz += nz * Hq
+    fwd_flops, bwd_flops = 4 * d * E, 10 * d * E
+    ms_step = total_ms / K
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    kernel_flops = {"fwd": 4 * d * E, "bwd_dq": 6 * d * E, "bwd_dkdv_band": 8 * d * Eb,
+                    "bwd_dkdv_anchor": 8 * d * Ea}
+    dominant = max(kernel_flops, key=lambda k_: avg[k_])
+    achieved = kernel_flops[dominant] / (avg[dominant] * 1e-3) / 1e12
+    kernel_symbol = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_band": "bwd_dkdv_kernel<band>",
+                     "bwd_dkdv_anchor": "bwd_dkdv_kernel<anchor>"}[dominant]
+    traffic = traffic_from_profiles(kernel_symbol)
+    result = dict(
+        metric="kept-tile TFLOP/s (fwd+bwd) and decode HBM GB/s; % of MI355X roofline",
+        value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=K, warmup=args.warmup,
+        ms_per_step=round(ms_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload="pythia160m-shaped SepLLM attention training step (index+fwd+bwd)",
+                    B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, a=a, n=n, p_sep=cfg["p_sep"], n_sep_ids=9,
+                    kept_tile_gflop_fwd=round(fwd_flops / 1e9, 3), kept_tile_gflop_bwd=round(bwd_flops / 1e9, 3),
+                    useful_gflop_fwd_bwd=round(14 * d * nnz / 1e9, 3), tile_efficiency=round(nnz / E, 4),
+                    wall_ms_per_step=round(wall / K * 1e3, 4)),
+        kernels_ms={nm: round(x, 5) for nm, x in avg.items()},
+        roofline=dict(kernel=kernel_symbol, bound="mfma", achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                      traffic=traffic, algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
+                      avg_launch_ms=round(avg[dominant], 5)),
+    )
+    return result, inp, E_seq0
+
+
+def decode_leg(args, torch, sa, synth):
+    cfg = synth.CONFIGS["sepcache_decode"]
+    B, Hq, Hkv, d, c, a, s, w = (cfg[x] for x in ("B", "Hq", "Hkv", "d", "c", "a", "s", "w"))
+    T = args.decode_steps
+    dev = torch.device("cuda:0")
+    r = synth.rng(cfg["seed"])
+    sep = synth.separator_ids(r, cfg["vocab"])
+    toks = torch.from_numpy(synth.token_ids_iid(r, (T, B), cfg["vocab"], sep, cfg["p_sep"])).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(cfg["seed"])
+    qs = torch.randn((T, B, Hq, d), device=dev, generator=gen).to(torch.bfloat16)
+    ks = torch.randn((T, B, Hkv, d), device=dev, generator=gen).to(torch.bfloat16)
+    vs = torch.randn((T, B, Hkv, d), device=dev, generator=gen).to(torch.bfloat16)
+    cos, sin = sa.rope_table(cfg["theta"], c, d)
+    cos, sin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    scale = d ** -0.5
+    cache = sa.SepCache(B, Hkv, d, c, a, s, w, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cache.workspace_bytes(Hq), dtype=torch.uint8, device=dev)
+
+    # untimed pass: cache lengths after every update (for the byte count)
+    lens = torch.empty((T, B, 4), dtype=torch.int32, device=dev)
+    for t in range(T):
+        cache.update(ks[t], vs[t], toks[t], sep)
+        lens[t].copy_(cache.state)
+    L = lens[:, :, :3].sum(-1).cpu().numpy().astype(np.int64)  # [T, B]
+
+    cache.init()
+    ev = Events()
+    stream = torch.cuda.current_stream().cuda_stream
+    marks = [ev.new(4) for _ in range(T)]
+    t0, t1 = ev.new(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for t in range(T):
+        m = marks[t]
+        ev.record(m[0], stream)
+        cache.update(ks[t], vs[t], toks[t], sep)
+        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=m[1:4])
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(t0, t1)
+    upd = np.array([ev.ms(m[0], m[1]) for m in marks])
+    dec = np.array([ev.ms(m[1], m[2]) for m in marks])
+    mrg = np.array([ev.ms(m[2], m[3]) for m in marks])
+    ev.close()
+    lo = min(1024, T // 4)
+    kv_bytes = (L * Hkv * d * 2 * 2).sum(axis=1)          # K and V rows, every slot, every kv head
+    q_bytes = B * Hq * d * 2
+    table_bytes = c * (d // 2) * 4 * 2
+    dec_bytes = kv_bytes + q_bytes + table_bytes            # per decode-kernel launch
+    gbs = dec_bytes[lo:].sum() / (dec[lo:].sum() * 1e-3) / 1e9
+    step_bytes = kv_bytes + 2 * q_bytes + B * Hkv * d * 2 * 2 + B * 4
+    step_ms = (upd + dec + mrg)[lo:]
+    traffic = traffic_from_profiles("decode_kernel")
+    return dict(
+        workload="SepCache streaming decode: B64, 32 q / 8 kv heads, d128, bf16, c=800 (a4 s64 w256), "
+                 "RoPE theta 500000 by slot, p_sep 0.08",
+        steps=T, steady_from=lo, mean_cached_slots=round(float(L[lo:].mean()), 1),
+        decode_kernel_us=round(float(dec[lo:].mean()) * 1e3, 3), merge_kernel_us=round(float(mrg[lo:].mean()) * 1e3, 3),
+        update_kernel_us=round(float(upd[lo:].mean()) * 1e3, 3),
+        us_per_step=round(float(step_ms.mean()) * 1e3, 3), loop_ms_total=round(total_ms, 3),
+        value=round(float(gbs), 1), unit="GB/s",
+        step_GBps=round(float(step_bytes[lo:].sum() / (step_ms.sum() * 1e-3) / 1e9), 1),
+        roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(float(gbs), 1), peak=PEAK_HBM_GBS,
+                      unit="GB/s", frac=round(float(gbs) / PEAK_HBM_GBS, 4), traffic=traffic,
+                      algorithmic_MB_per_launch=round(float(dec_bytes[lo:].mean()) / 1e6, 3)),
+    )
+
+
+def cpu_leg(args, inp, E_seq0):
+    from oracle import attention
+    cfg = inp["cfg"]
+    a, n, d, S, Hq = cfg["a"], cfg["n"], cfg["d"], cfg["S"], cfg["Hq"]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+
+    def run(nh):
+        sl = (slice(0, 1), slice(0, nh))
+        t = time.perf_counter()
+        attention.attention_forward(inp["qf"][sl], inp["kf"][sl], inp["vf"][sl], inp["tok"][:1], inp["sep"],
+                                    a, n, scale=inp["scale"])
+        attention.attention_backward(inp["qf"][sl], inp["kf"][sl], inp["vf"][sl], inp["dof"][sl],
+                                     inp["tok"][:1], inp["sep"], a, n, scale=inp["scale"])
+        return time.perf_counter() - t
+
+    t1 = run(1)
+    nh = int(max(1, min(Hq, round(args.cpu_seconds / max(t1, 1e-3)))))
+    tn = run(nh) if nh > 1 else t1
+    # kept-tile work of the sample: sequence 0's schedule, nh heads
+    flops = (4 + 10) * d * E_seq0 * nh
+    return dict(value=round(flops / tn / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"fp64 numpy oracle fwd+bwd of sequence 0, heads 0..{nh - 1} of the same inputs "
+                       f"({nh} of {cfg['B'] * Hq} (sequence, head) pairs), {tn:.1f} s",
+                seconds=round(tn, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every configuration of this "
+              f"workload fits one MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_sepattn_amd as sa
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sa.load_library()
+    log("prefill/training leg ...")
+    result, inp, E_seq0 = prefill_leg(args, torch, sa, synth)
+    log(f"  {result['value']} TFLOP/s, {result['ms_per_step']} ms/step")
+    if not args.no_decode:
+        log("decode leg ...")
+        result["decode"] = decode_leg(args, torch, sa, synth)
+        log(f"  {result['decode']['value']} GB/s decode kernel")
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_leg(args, inp, E_seq0)
+        log(f"  {result['cpu_baseline']['value']} TFLOP/s on {result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

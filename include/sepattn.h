@@ -212,6 +212,14 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
                     const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* sepcache_decode with per-kernel timing: `events` is a HOST array of
+ * n_events >= 3 hipEvent_t (as void*), recorded on `stream` before the decode
+ * kernel, after it, and after the kernel that merges its chunk partials.
+ * Results are identical to sepcache_decode. */
+int sepcache_decode_profiled(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                             const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
+                             void* stream, void* const* events, int n_events);
+
 /* Host helper: cos/sin tables of the rotate-half rotary embedding,
  * cos_out[p*(d/2)+m] = cos(p * theta^(-2m/d)) (likewise sin), for p < c and
  * m < d/2, evaluated in double precision and rounded once to float.

@@ -57,7 +57,8 @@ class _Cache(ctypes.Structure):
 EXPORTS = ["sepattn_strerror", "sepattn_index_bytes", "sepattn_index_bind", "sepattn_build_index",
            "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepattn_bwd_profiled",
            "sepcache_init", "sepcache_update",
-           "sepcache_decode_workspace", "sepcache_decode", "sepattn_rope_table_host"]
+           "sepcache_decode_workspace", "sepcache_decode", "sepcache_decode_profiled",
+           "sepattn_rope_table_host"]
 
 
 def load_library(path=None):
@@ -98,6 +99,8 @@ def load_library(path=None):
     L.sepcache_decode_workspace.argtypes = [ctypes.POINTER(_Cache), i32]
     L.sepcache_decode.restype = i32
     L.sepcache_decode.argtypes = [ctypes.POINTER(_Cache), vp, i32, vp, vp, f32, vp, vp, sz, vp]
+    L.sepcache_decode_profiled.restype = i32
+    L.sepcache_decode_profiled.argtypes = [ctypes.POINTER(_Cache), vp, i32, vp, vp, f32, vp, vp, sz, vp, vp, i32]
     L.sepattn_rope_table_host.restype = i32
     L.sepattn_rope_table_host.argtypes = [ctypes.c_double, i32, i32, vp, vp]
     if path is None:
@@ -287,7 +290,9 @@ class SepCache:
     def workspace_bytes(self, Hq):
         return load_library().sepcache_decode_workspace(ctypes.byref(self.st), Hq)
 
-    def decode(self, q, rope_cos, rope_sin, scale=None, o=None, ws=None):
+    def decode(self, q, rope_cos, rope_sin, scale=None, o=None, ws=None, events=None):
+        """Decode attention of the newest token; ``events``: optional 3
+        hipEvent_t handles recorded around the two kernels."""
         B, Hq, d = q.shape
         _need(q, "q", torch.bfloat16, (self.B, Hq, self.d))
         _need(rope_cos, "rope_cos", torch.float32, (self.c, self.d // 2))
@@ -302,6 +307,11 @@ class SepCache:
             if self._ws is None or self._ws.numel() < nbytes:
                 self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
             ws = self._ws
-        _check(L.sepcache_decode(ctypes.byref(self.st), _ptr(q), Hq, _ptr(rope_cos), _ptr(rope_sin),
-                                 float(scale), _ptr(o), _ptr(ws), ws.numel(), _stream()), "sepcache_decode")
+        args = (ctypes.byref(self.st), _ptr(q), Hq, _ptr(rope_cos), _ptr(rope_sin), float(scale), _ptr(o),
+                _ptr(ws), ws.numel(), _stream())
+        if events is None:
+            _check(L.sepcache_decode(*args), "sepcache_decode")
+        else:
+            arr = (ctypes.c_void_p * len(events))(*events)
+            _check(L.sepcache_decode_profiled(*args, arr, len(events)), "sepcache_decode_profiled")
         return o

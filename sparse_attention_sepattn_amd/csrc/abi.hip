@@ -182,9 +182,9 @@ size_t sepcache_decode_workspace(const sepcache* cache, int Hq) {
   return decode_workspace_bytes(*cache, Hq);
 }
 
-int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
-                    const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
-                    void* stream) {
+static int decode_common(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                         const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
+                         void* stream, hipEvent_t* ev) {
   int st = check_cache(cache);
   if (st != SEPATTN_OK) return st;
   if (!q || !rope_cos || !rope_sin || !o || Hq < 1 || Hq % cache->Hkv != 0 || !isfinite(scale))
@@ -193,7 +193,22 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
   if (G > kMaxDecodeGroup || (G & (G - 1)) != 0) return SEPATTN_EUNSUPPORTED;
   if (!ws || ((uintptr_t)ws & 255) != 0) return SEPATTN_EINVAL;
   if (ws_bytes < decode_workspace_bytes(*cache, Hq)) return SEPATTN_EWORKSPACE;
-  return to_status(launch_decode(*cache, q, Hq, rope_cos, rope_sin, scale, o, ws, (hipStream_t)stream));
+  return to_status(
+      launch_decode(*cache, q, Hq, rope_cos, rope_sin, scale, o, ws, (hipStream_t)stream, ev));
+}
+
+int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                    const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return decode_common(cache, q, Hq, rope_cos, rope_sin, scale, o, ws, ws_bytes, stream, nullptr);
+}
+
+int sepcache_decode_profiled(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                             const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
+                             void* stream, void* const* events, int n_events) {
+  if (!events || n_events < 3 || !events[0] || !events[1] || !events[2]) return SEPATTN_EINVAL;
+  return decode_common(cache, q, Hq, rope_cos, rope_sin, scale, o, ws, ws_bytes, stream,
+                       (hipEvent_t*)events);
 }
 
 int sepattn_rope_table_host(double theta, int c, int d, float* cos_out, float* sin_out) {

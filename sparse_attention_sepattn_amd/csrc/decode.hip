@@ -215,27 +215,32 @@ size_t decode_workspace_bytes(const sepcache& c, int Hq) {
 }
 
 template <int D, int G>
-static hipError_t launch_decode_t(const DecArgs& a, int B, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecArgs& a, int B, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3(a.nsplit, a.Hkv, B), dim3(kDecThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * a.Hq), dim3(D), 0, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecArgs& a, int B, int G, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecArgs& a, int B, int G, hipStream_t stream, hipEvent_t* ev) {
   switch (G) {
-    case 1: return launch_decode_t<D, 1>(a, B, stream);
-    case 2: return launch_decode_t<D, 2>(a, B, stream);
-    case 4: return launch_decode_t<D, 4>(a, B, stream);
-    case 8: return launch_decode_t<D, 8>(a, B, stream);
+    case 1: return launch_decode_t<D, 1>(a, B, stream, ev);
+    case 2: return launch_decode_t<D, 2>(a, B, stream, ev);
+    case 4: return launch_decode_t<D, 4>(a, B, stream, ev);
+    case 8: return launch_decode_t<D, 8>(a, B, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* rope_cos,
-                         const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream) {
+                         const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream,
+                         hipEvent_t* ev) {
   DecArgs a;
   a.k = (const uint16_t*)c.k;
   a.v = (const uint16_t*)c.v;
@@ -251,8 +256,8 @@ hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* 
   a.nsplit = n_splits(c.c);
   a.scale_log2 = scale * 1.4426950408889634f;
   const int G = Hq / c.Hkv;
-  if (c.d == 64) return launch_decode_d<64>(a, c.B, G, stream);
-  return launch_decode_d<128>(a, c.B, G, stream);
+  if (c.d == 64) return launch_decode_d<64>(a, c.B, G, stream, ev);
+  return launch_decode_d<128>(a, c.B, G, stream, ev);
 }
 
 }  // namespace sepattn

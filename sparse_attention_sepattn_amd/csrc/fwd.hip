@@ -29,18 +29,19 @@ struct FwdArgs {
 constexpr int kFwdThreads = 256;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kFwdThreads) fwd_kernel(FwdArgs p) {
+__global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kernel(FwdArgs p) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
+  typedef TileRegs<T, D, kFwdThreads> Regs;
   typedef typename Tr::frag frag;
   constexpr int EPL = Tr::EPL;
   constexpr int KSTEP = Tr::KSTEP;
-  constexpr int NQF = D / KSTEP;      // Q fragments per lane
-  constexpr int NDB = D / 32;         // 32-row blocks of O^T
-  constexpr int NPS = kKTile / KSTEP; // MFMA steps of P V per tile
+  constexpr int NQF = D / KSTEP;   // Q fragments per lane
+  constexpr int NDB = D / 32;      // 32-row blocks of O^T
+  constexpr int SPB = 32 / KSTEP;  // MFMA steps per 32-key block
 
-  __shared__ __attribute__((aligned(16))) T Ks[G::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) T Vt[G::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) T Ks[2][G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][G::ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,6 +69,34 @@ __global__ void __launch_bounds__(kFwdThreads) fwd_kernel(FwdArgs p) {
   const int32_t* anc = p.anchor_pos + (size_t)b * p.S;
   const uint8_t* sepf = p.is_sep + (size_t)b * p.S;
 
+  auto src_of = [&](int t) {
+    RowSrc r;
+    if (t < n_at) {
+      r.anchor = anc;
+      r.base = t * kKTile;
+      r.limit = n_anchor;
+    } else {
+      r.anchor = nullptr;
+      r.base = (kb + t - n_at) * kKTile;
+      r.limit = p.S;
+    }
+    return r;
+  };
+  auto sep_flag = [&](int t) -> int {
+    if (t < n_at) return 0;
+    const int j = (kb + t - n_at) * kKTile + lane;
+    return j < p.S ? (int)sepf[j] : 0;
+  };
+
+  // prologue: tile 0 in flight, rows of tile 1 resolved
+  Regs rk, rv;
+  int rows[Regs::NU];
+  Regs::rows(rows, src_of(0), tid);
+  rk.issue(Kg, rows, tid);
+  rv.issue(Vg, rows, tid);
+  int sflag = sep_flag(0);
+  if (n_tiles > 1) Regs::rows(rows, src_of(1), tid);
+
   frag qf[NQF];
 #pragma unroll
   for (int c = 0; c < NQF; ++c) {
@@ -85,65 +114,52 @@ __global__ void __launch_bounds__(kFwdThreads) fwd_kernel(FwdArgs p) {
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const bool anchor_tile = t < n_at;
-    const int kt = kb + (t - n_at);
-    RowSrc src;
-    if (anchor_tile) {
-      src.anchor = anc;
-      src.base = t * kKTile;
-      src.limit = n_anchor;
-    } else {
-      src.anchor = nullptr;
-      src.base = kt * kKTile;
-      src.limit = p.S;
+    const int buf = t & 1;
+    rk.store(Ks[buf], tid);
+    rv.store(Vs[buf], tid);
+    const uint64_t sepbits = __ballot(sflag != 0);
+    __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
+    if (t + 1 < n_tiles) {
+      rk.issue(Kg, rows, tid);
+      rv.issue(Vg, rows, tid);
+      sflag = sep_flag(t + 1);
+      if (t + 2 < n_tiles) Regs::rows(rows, src_of(t + 2), tid);
     }
-    __syncthreads();
-    load_k_tile<T, D, kFwdThreads>(Ks, Kg, src, tid);
-    load_vt_tile<T, D, kFwdThreads>(Vt, Vg, src, tid);
-    uint64_t sepbits = 0;
-    if (!anchor_tile) {
-      const int j = kt * kKTile + lane;
-      sepbits = __ballot(j < p.S && sepf[j] != 0);
-    }
-    __syncthreads();
+    const T* K = Ks[buf];
+    const T* V = Vs[buf];
 
     // S^T = K Q^T for the two 32-key halves of the tile
     f32x16 sacc[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       f32x16 acc = f32x16{};
-      const T* krow = Ks + (32 * k2 + qc) * G::KSTR + EPL * hh;
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(*(const frag*)(krow + c * KSTEP), qf[c], acc);
+      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(read_x<T, D>(K, k2, c, lane), qf[c], acc);
       sacc[k2] = acc;
     }
 
-    // scale and mask
+    // scale and mask (bit r of vis: key r of the tile is visible to this row)
+    const bool anchor_tile = t < n_at;
     bool full;
+    uint64_t vis;
     if (anchor_tile) {
-      full = (t + 1) * kKTile <= n_anchor;
+      const int nv = n_anchor - t * kKTile;
+      full = nv >= kKTile;
+      vis = bit_range(0, nv - 1);
     } else {
-      const int c0 = kt * kKTile;
+      const int c0 = (kb + t - n_at) * kKTile;
       full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
+      vis = band_visible(iq, c0, lo, p.S, p.a, p.n, sepbits);
     }
+    vis >>= 4 * hh;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      const uint32_t vw = (uint32_t)(vis >> (32 * k2));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float s = sacc[k2][i] * p.scale_log2;
-        if (!full) {
-          const int r = 32 * k2 + acc_row(i, hh);
-          bool vis;
-          if (anchor_tile) {
-            vis = t * kKTile + r < n_anchor;
-          } else {
-            const int j = kt * kKTile + r;
-            vis = j < p.S && j >= lo && j <= iq &&
-                  (j < p.a || ((sepbits >> r) & 1ull) || iq - j < p.n);
-          }
-          s = vis ? s : -INFINITY;
-        }
-        sacc[k2][i] = s;
+        float sv = sacc[k2][i] * p.scale_log2;
+        if (!full && !((vw >> (((i >> 2) << 3) + (i & 3))) & 1u)) sv = -INFINITY;
+        sacc[k2][i] = sv;
       }
     }
 
@@ -172,22 +188,14 @@ __global__ void __launch_bounds__(kFwdThreads) fwd_kernel(FwdArgs p) {
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int s = 0; s < NPS; ++s) {
-      const int k2 = s / (32 / KSTEP);
-      const int sl = s % (32 / KSTEP);
-      frag pf;
-      if constexpr (EPL == 8) {
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)sacc[k2][sl * 8 + j];
-      } else {
-        pf = sacc[k2][sl];
-      }
+      for (int sl = 0; sl < SPB; ++sl) {
+        const frag pf = acc_frag<T>(sacc[k2], sl);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const frag vf = *(const frag*)(Vt + (32 * db + qc) * G::VSTR + 32 * k2 + sl * 2 * EPL + hh * EPL);
-        oacc[db] = Tr::mfma(vf, pf, oacc[db]);
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = Tr::mfma(read_xt<T, D>(V, k2, sl, 32 * db, lane), pf, oacc[db]);
       }
-    }
   }
 
   // normalise and store

@@ -134,20 +134,24 @@ index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
     f[6] = q0;
     f[7] = 0;
   }
+  // 8 lanes per key tile, each counting 16 of the 128 rows
   uint8_t* cls = tile_class + ((size_t)b * QT + qi) * KT;
-  for (int kj = threadIdx.x; kj < KT; kj += blockDim.x) {
+  const int sub = threadIdx.x & 7;
+  for (int base = 0; base < KT; base += blockDim.x / 8) {
+    const int kj = base + threadIdx.x / 8;
     const int c0 = kj * kKTile;
     const int c1 = min(c0 + kKTile - 1, S - 1);
-    uint8_t c;
-    if (c0 > q1) {
-      c = 0;  // entirely above the diagonal
-    } else {
-      int total = 0;
-      for (int i = q0; i <= q1; ++i) total += row_count(i, c0, c1, a, n, pre);
-      const int full = (q1 - q0 + 1) * (c1 - c0 + 1);
-      c = total == 0 ? 0 : (total == full ? 2 : 1);
+    int total = 0;
+    if (kj < KT && c0 <= q1) {
+      for (int i = q0 + sub; i <= q1; i += 8) total += row_count(i, c0, c1, a, n, pre);
     }
-    cls[kj] = c;
+    total += __shfl_xor(total, 1, 64);
+    total += __shfl_xor(total, 2, 64);
+    total += __shfl_xor(total, 4, 64);
+    if (kj < KT && sub == 0) {
+      const int full = (q1 - q0 + 1) * (c1 - c0 + 1);
+      cls[kj] = total == 0 ? 0 : (total == full ? 2 : 1);
+    }
   }
 }
 

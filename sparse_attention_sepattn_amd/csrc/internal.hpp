@@ -36,7 +36,9 @@ hipError_t launch_cache_init(const sepcache& c, hipStream_t stream);
 hipError_t launch_cache_update(const sepcache& c, const void* k_new, const void* v_new,
                                const int32_t* tok_new, const SepSet& sep, hipStream_t stream);
 size_t decode_workspace_bytes(const sepcache& c, int Hq);
+// `ev` (nullable): 3 events, before the decode kernel, after it, after the merge.
 hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* rope_cos,
-                         const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream);
+                         const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream,
+                         hipEvent_t* ev);
 
 }  // namespace sepattn

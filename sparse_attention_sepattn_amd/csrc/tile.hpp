@@ -1,14 +1,26 @@
-// MFMA traits and LDS tile loaders shared by the attention kernels.
+// MFMA traits, LDS tile loaders and operand readers shared by the attention
+// kernels.
 //
-// Formulation.  A workgroup owns 128 query rows (4 waves x 32 rows).  Scores
-// are computed transposed, S^T = K Q^T, with v_mfma 32x32 (keys on the M axis,
-// queries on the N axis), so each lane holds one query column and the softmax
-// statistics of that query stay in the lane (plus its partner 32 lanes away).
-// The output is accumulated transposed as well, O^T = V^T P^T, so P^T feeds the
-// MFMA B operand straight from the score registers; only V has to be stored
-// transposed in LDS.  The MFMA contraction index may be permuted freely as long
-// as both operands use the same permutation: the transposed V tile is written
-// in the key order the score registers hold ("kpos").
+// Formulation.  A query-major workgroup owns 128 query rows (4 waves x 32
+// rows).  Scores are computed transposed, S^T = K Q^T, with v_mfma 32x32
+// (keys on the M axis, queries on the N axis), so each lane holds one query
+// column and the softmax statistics of that query stay in the lane (plus its
+// partner 32 lanes away).  The output is accumulated transposed as well,
+// O^T = V^T P^T, so P^T feeds the MFMA B operand straight from the score
+// registers.  The A operand V^T is read from the row-major V tile in LDS with
+// the gfx950 transpose read (ds_read_b64_tr_b16): within each 16-lane group,
+// output lane 4a+c receives element c of the 8-byte chunks addressed by lanes
+// a, 4+a, 8+a, 12+a.  Addressing row r0+4h+(s>>2), column c0+16*(g&1)+4*(s&3)
+// from source lane s of group g therefore gives output lane l the column
+// c0+(l&31) of rows r0+4h+k, k = 0..3: the A operand of X^T for a row-major X.
+// The MFMA contraction index may be permuted freely as long as both operands
+// use the same permutation; the rows read here follow the order the score
+// registers hold keys in (acc_row below).  fp32 tiles need no transpose read:
+// one element per lane is a plain LDS read.
+//
+// Every tile is stored row-major in LDS (16-byte chunks XOR-swizzled by row,
+// see TileGeom) and loaded through registers so the next tile's global loads
+// are in flight while the current tile computes.
 #pragma once
 
 #include "common.hpp"
@@ -23,8 +35,7 @@ struct Traits<__bf16> {
   static constexpr int EPL = 8;    // operand elements per lane per MFMA
   static constexpr int KSTEP = 16; // MFMA contraction depth
   static constexpr int VEC = 8;    // elements per 16-byte chunk
-  static constexpr int KPAD = 8;   // LDS row padding of the K tile (elements)
-  static constexpr int VPAD = 8;   // LDS row padding of the transposed V tile
+  static constexpr int PAD = 8;    // LDS row padding (elements)
   typedef bf16x8 frag;
   static __device__ __forceinline__ f32x16 mfma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -36,40 +47,48 @@ struct Traits<float> {
   static constexpr int EPL = 1;
   static constexpr int KSTEP = 2;
   static constexpr int VEC = 4;
-  static constexpr int KPAD = 4;
-  static constexpr int VPAD = 4;
+  static constexpr int PAD = 4;
   typedef float frag;
   static __device__ __forceinline__ f32x16 mfma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
 };
 
-// Key held by accumulator element i (0..15) of a 32x32 MFMA result in lane
-// half hh (lane / 32): rows 8*(i/4) + 4*hh + i%4.
+// Row held by accumulator element i (0..15) of a 32x32 MFMA result in lane
+// half hh (lane / 32): 8*(i/4) + 4*hh + i%4.
 __device__ __forceinline__ int acc_row(int i, int hh) { return ((i >> 2) << 3) + (hh << 2) + (i & 3); }
 
-// Column of tile key r (0..63) in the transposed V tile.
-template <int EPL>
-__device__ __forceinline__ int kpos_of(int r) {
-  const int kb2 = r >> 5, rr = r & 31;
-  const int idx = ((rr >> 3) << 2) | (rr & 3);
-  const int hh = (rr >> 2) & 1;
-  return 32 * kb2 + (idx / EPL) * (2 * EPL) + hh * EPL + (idx % EPL);
+// 16-byte chunks of a row are stored XOR-swizzled by the row index (no
+// padding).  The row-major read of 32 consecutive rows at one chunk and the
+// transpose read of 4 consecutive rows x 32 bytes both touch distinct banks:
+//   >= 16 chunks per row: c ^ f(r), f bijective on r % 16, and the 4 rows of
+//   an aligned group map a chunk pair {2k, 2k+1} to 8 distinct chunks;
+//   8 chunks per row (two rows per 256-byte bank line): c ^ g(r) with g
+//   bijective on (r >> 1) % 8 and rows r, r+2 of an aligned group differing
+//   in a bit >= 1.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int swz8(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
 }
 
 template <typename T, int D>
 struct TileGeom {
-  static constexpr int KSTR = D + Traits<T>::KPAD;          // K tile row stride (elements)
-  static constexpr int VSTR = kKTile + Traits<T>::VPAD;     // V^T tile row stride (elements)
-  static constexpr int K_ELEMS = kKTile * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int CH = D / Traits<T>::VEC;             // 16-byte chunks per row
+  static constexpr int VEC = Traits<T>::VEC;
+  static constexpr int CH = D / VEC;       // 16-byte chunks per row
+  static constexpr int ELEMS = kKTile * D; // one 64-row tile
+  // element offset of (row, col) in a swizzled tile
+  static __device__ __forceinline__ int at(int row, int col) {
+    const int f = CH >= 16 ? swz16(row) : swz8(row);
+    return row * D + (((col / VEC) ^ f) & (CH - 1)) * VEC + (col % VEC);
+  }
 };
 
 // Source row of tile row r: a gathered anchor (anchor list entry base + r,
-// valid below `limit`) or a plain key tile (row base + r, valid below S).
+// valid below `limit`) or a plain key/query tile (row base + r, valid below
+// `limit`).
 struct RowSrc {
-  const int32_t* anchor;  // nullptr for a plain key tile
+  const int32_t* anchor;  // nullptr for a plain tile
   int base;
   int limit;
   __device__ __forceinline__ int row(int r) const {
@@ -79,62 +98,112 @@ struct RowSrc {
   }
 };
 
-// K tile -> Ks[r][c] (row-major, padded).  Invalid rows are zero.
+// One 64-row tile of a [rows, D] tensor, global -> registers -> LDS.  Thread
+// tid owns NU 16-byte chunks: unit u is row tid/CH + (NT/CH)*u, chunk tid%CH,
+// so consecutive lanes read consecutive chunks of a row.
 template <typename T, int D, int NT>
-__device__ __forceinline__ void load_k_tile(T* __restrict__ Ks, const T* __restrict__ Kg, RowSrc src,
-                                            int tid) {
+struct TileRegs {
   typedef TileGeom<T, D> G;
-  constexpr int VEC = Traits<T>::VEC;
-  for (int u = tid; u < kKTile * G::CH; u += NT) {
-    const int r = u / G::CH, cc = u % G::CH;
-    const int row = src.row(r);
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row >= 0) val = *(const u32x4*)(Kg + (size_t)row * D + cc * VEC);
-    *(u32x4*)(Ks + r * G::KSTR + cc * VEC) = val;
+  static constexpr int NU = kKTile * G::CH / NT;
+  static_assert(NU * NT == kKTile * G::CH, "tile must split evenly over the workgroup");
+  u32x4 r[NU];
+
+  static __device__ __forceinline__ int row_of(int tid, int u) { return tid / G::CH + (NT / G::CH) * u; }
+
+  // source rows of this thread's units (anchor tiles read the anchor list)
+  __device__ __forceinline__ static void rows(int* out, RowSrc src, int tid) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) out[u] = src.row(row_of(tid, u));
+  }
+  __device__ __forceinline__ void issue(const T* __restrict__ g, const int* srow, int tid) {
+    const int cc = tid % G::CH;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (srow[u] >= 0) v = *(const u32x4*)(g + (size_t)srow[u] * D + cc * Traits<T>::VEC);
+      r[u] = v;
+    }
+  }
+  __device__ __forceinline__ void store(T* __restrict__ s, int tid) const {
+    const int cc = tid % G::CH;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) *(u32x4*)(s + G::at(row_of(tid, u), cc * Traits<T>::VEC)) = r[u];
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
+}
+
+// A operand of X^T for MFMA step `sl` over the 32-row block `k2` of a
+// row-major swizzled LDS tile X: lane (m = lane&31, h = lane>>5) gets column
+// c0 + m of the rows the score accumulators hold for that step.
+// bf16 (16 rows per step): rows 32*k2 + 16*sl + 8*(j/4) + 4h + j%4, j = 0..7.
+// fp32 (2 rows per step):  row 32*k2 + acc_row(sl, h).
+template <typename T, int D>
+__device__ __forceinline__ typename Traits<T>::frag read_xt(const T* X, int k2, int sl, int c0, int lane) {
+  typedef TileGeom<T, D> G;
+  if constexpr (Traits<T>::EPL == 8) {
+    const int grp = lane >> 4, s = lane & 15;
+    const int h = grp >> 1;
+    const int col = c0 + 16 * (grp & 1) + 4 * (s & 3);
+    const int row = 32 * k2 + 16 * sl + 4 * h + (s >> 2);
+    const s16x4 lo = lds_read_tr16(X + G::at(row, col));
+    const s16x4 hi = lds_read_tr16(X + G::at(row + 8, col));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return X[G::at(32 * k2 + acc_row(sl, lane >> 5), c0 + (lane & 31))];
   }
 }
 
-// V tile -> Vt[d][kpos(r)] (transposed, padded).  Invalid rows are zero.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void load_vt_tile(T* __restrict__ Vt, const T* __restrict__ Vg, RowSrc src,
-                                             int tid) {
+// A operand of X (row-major) for the contraction over columns: lane (row
+// m = lane&31 of the 32-row block `rb`, h) gets columns c*KSTEP + EPL*h ..
+template <typename T, int D>
+__device__ __forceinline__ typename Traits<T>::frag read_x(const T* X, int rb, int c, int lane) {
   typedef TileGeom<T, D> G;
-  if constexpr (Traits<T>::EPL == 8) {
-    // unit = (group gi of 8 keys that are adjacent in kpos order, chunk cc)
-    for (int u = tid; u < 8 * G::CH; u += NT) {
-      const int gi = u & 7, cc = u >> 3;
-      const int kb2 = gi >> 2, sl = (gi >> 1) & 1, hh = gi & 1;
-      u32x4 rows[8];
+  constexpr int EPL = Traits<T>::EPL;
+  const int row = 32 * rb + (lane & 31);
+  const int col = c * Traits<T>::KSTEP + EPL * (lane >> 5);
+  return *(const typename Traits<T>::frag*)(X + G::at(row, col));
+}
+
+// Bits [lo, hi] of a 64-bit word (lo, hi clamped to [0, 63]; empty if hi < lo).
+__device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 63 ? 63 : hi;
+  if (hi < lo) return 0ull;
+  return (~0ull >> (63 - hi)) & (~0ull << lo);
+}
+
+// Keys c0 .. c0+63 of the band that query row iq sees (bit r = key c0 + r):
+// keys in [lo, min(iq, S-1)] that are initial (< a) or separators (sepbits),
+// plus the window [max(lo, iq - n + 1), min(iq, S-1)].
+__device__ __forceinline__ uint64_t band_visible(int iq, int c0, int lo, int S, int a, int n,
+                                                 uint64_t sepbits) {
+  const int hi = (iq < S - 1 ? iq : S - 1) - c0;
+  const int w0 = (lo > iq - n + 1 ? lo : iq - n + 1) - c0;
+  return bit_range(w0, hi) | ((sepbits | bit_range(0, a - 1 - c0)) & bit_range(lo - c0, hi));
+}
+
+// B operand of step s from a 32x32 score accumulator: elements s*EPL..+EPL.
+template <typename T>
+__device__ __forceinline__ typename Traits<T>::frag acc_frag(const f32x16& a, int s);
+
+template <>
+__device__ __forceinline__ bf16x8 acc_frag<__bf16>(const f32x16& a, int s) {
+  bf16x8 f;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int r = 32 * kb2 + 16 * sl + 4 * hh + jj + (jj >= 4 ? 4 : 0);
-        const int row = src.row(r);
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (row >= 0) val = *(const u32x4*)(Vg + (size_t)row * D + cc * 8);
-        rows[jj] = val;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x4 out;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x0 = rows[2 * w][e >> 1], x1 = rows[2 * w + 1][e >> 1];
-          out[w] = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
-        }
-        *(u32x4*)(Vt + (cc * 8 + e) * G::VSTR + 8 * gi) = out;
-      }
-    }
-  } else {
-    for (int u = tid; u < kKTile * G::CH; u += NT) {
-      const int r = u / G::CH, cc = u % G::CH;
-      const int row = src.row(r);
-      f32x4 val = {0.f, 0.f, 0.f, 0.f};
-      if (row >= 0) val = *(const f32x4*)((const float*)Vg + (size_t)row * D + cc * 4);
-      const int kp = kpos_of<1>(r);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ((float*)Vt)[(cc * 4 + e) * G::VSTR + kp] = val[e];
-    }
-  }
+  for (int j = 0; j < 8; ++j) f[j] = (__bf16)a[s * 8 + j];
+  return f;
+}
+
+template <>
+__device__ __forceinline__ float acc_frag<float>(const f32x16& a, int s) {
+  return a[s];
 }
 
 }  // namespace sepattn
