@@ -17,10 +17,10 @@ measured step time (index build included).  The useful-entry count
 (visible mask entries) and the tile efficiency are reported beside it.
 
 roofline: the kernel with the largest average duration, its algorithmic
-FLOPs on the same schedule (2 GEMMs per kept tile for the forward, 3 for the
-query-major dQ, 4 for the key-major dK/dV) over its duration measured with
-HIP events on the launch stream during the timed steps, against the bf16
-dense MFMA peak.
+FLOPs on the same schedule (2 GEMMs per kept entry for the forward; 7 for the
+backward main kernel: S, dP, dV, dK key-major and S, dP, dQ query-major) over
+its duration measured with HIP events on the launch stream during the timed
+steps, against the bf16 dense MFMA peak.
 
 decode: the streaming SepCache workload (B=64, 32 q / 8 kv heads, d=128,
 c=800 = 4 initial + 64 separator slots + a 256-token window, RoPE theta
@@ -158,14 +158,14 @@ def prefill_leg(args, torch, sa, synth):
         if marks is not None:
             ev.record(marks[2], stream)
         sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws,
-               events=None if marks is None else marks[3:8])
+               events=None if marks is None else marks[3:7])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    marks = [ev.new(8) for _ in range(K)]
+    marks = [ev.new(7) for _ in range(K)]
     t_start, t_end = ev.new(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -176,15 +176,14 @@ def prefill_leg(args, torch, sa, synth):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev.ms(t_start, t_end)
-    names = ["index", "fwd", "bwd_rowsum", "bwd_dkdv_anchor", "bwd_dkdv_band", "bwd_dq"]
+    names = ["index", "fwd", "bwd_rowsum", "bwd_main", "bwd_finalize"]
     seg = {nm: [] for nm in names}
     for m in marks:
         seg["index"].append(ev.ms(m[0], m[1]))
         seg["fwd"].append(ev.ms(m[1], m[2]))
         seg["bwd_rowsum"].append(ev.ms(m[3], m[4]))
-        seg["bwd_dkdv_anchor"].append(ev.ms(m[4], m[5]))
-        seg["bwd_dkdv_band"].append(ev.ms(m[5], m[6]))
-        seg["bwd_dq"].append(ev.ms(m[6], m[7]))
+        seg["bwd_main"].append(ev.ms(m[4], m[5]))
+        seg["bwd_finalize"].append(ev.ms(m[5], m[6]))
     avg = {nm: float(np.mean(x)) for nm, x in seg.items()}
     ev.close()
 
@@ -205,12 +204,12 @@ def prefill_leg(args, torch, sa, synth):
     ms_step = total_ms / K
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
-    kernel_flops = {"fwd": 4 * d * E, "bwd_dq": 6 * d * E, "bwd_dkdv_band": 8 * d * Eb,
-                    "bwd_dkdv_anchor": 8 * d * Ea}
+    # GEMMs each kernel performs per kept entry: forward 2; backward main 7
+    # (dK/dV: S, dP, dV, dK; dQ: S, dP, dQ)
+    kernel_flops = {"fwd": 4 * d * E, "bwd_main": 8 * d * (Ea + Eb) + 6 * d * E}
     dominant = max(kernel_flops, key=lambda k_: avg[k_])
     achieved = kernel_flops[dominant] / (avg[dominant] * 1e-3) / 1e12
-    kernel_symbol = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_band": "bwd_dkdv_kernel<band>",
-                     "bwd_dkdv_anchor": "bwd_dkdv_kernel<anchor>"}[dominant]
+    kernel_symbol = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}[dominant]
     traffic = traffic_from_profiles(kernel_symbol)
     result = dict(
         metric="kept-tile TFLOP/s (fwd+bwd) and decode HBM GB/s; % of MI355X roofline",

@@ -52,7 +52,7 @@ extern "C" {
 
 /* status codes */
 #define SEPATTN_OK 0
-#define SEPATTN_EINVAL 1       /* null pointer, negative or zero size, a < 0, n < 1, Hq % Hkv != 0, ... */
+#define SEPATTN_EINVAL 1       /* null pointer, negative or zero size, a < 0, n < 1, Hq % Hkv != 0, scale <= 0, ... */
 #define SEPATTN_EUNSUPPORTED 2 /* dtype / head-dim combination not built (d must be 64 or 128) */
 #define SEPATTN_ECAPACITY 3    /* SepCache capacities: need w >= 1, s >= 0, a >= 0 and c > a + s + w */
 #define SEPATTN_EWORKSPACE 4   /* workspace smaller than the matching *_workspace() query */
@@ -132,7 +132,7 @@ int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* s
 /* Attention over the full sequence (training / prefill)                     */
 /* ------------------------------------------------------------------------ */
 
-/* Forward.  q [B,Hq,S,d], k/v [B,Hkv,S,d] of `dtype`, scale (e.g. 1/sqrt(d)),
+/* Forward.  q [B,Hq,S,d], k/v [B,Hkv,S,d] of `dtype`, scale > 0 (e.g. 1/sqrt(d)),
  * idx built for these B, S.  Writes o [B,Hq,S,d] (dtype) and lse [B,Hq,S]
  * fp32 = natural log of each row's softmax normaliser of the scaled scores.
  * Supported: dtype F32 or BF16 with d in {64, 128}.  No workspace. */
@@ -154,11 +154,12 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 void* stream);
 
 /* sepattn_bwd with per-kernel timing: `events` is a HOST array of n_events
- * >= 5 hipEvent_t (created by the caller, passed as void*).  events[0] is
+ * >= 4 hipEvent_t (created by the caller, passed as void*).  events[0] is
  * recorded on `stream` before the first kernel and events[i] after the i-th
- * of the four kernels: (1) row sums D = rowsum(dO * O), (2) key-major dK/dV
- * over gathered anchor tiles, (3) key-major dK/dV over band tiles, (4)
- * query-major dQ.  Results are identical to sepattn_bwd. */
+ * of the three kernels: (1) row sums D = rowsum(dO * O), (2) the main kernel
+ * (key-major dK/dV over gathered anchor tiles and over band tiles, and
+ * query-major dQ, as one grid of independent work items), (3) the sum of the
+ * anchor rows' partials.  Results are identical to sepattn_bwd. */
 int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
                          const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,

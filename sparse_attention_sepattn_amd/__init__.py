@@ -221,7 +221,7 @@ def bwd_workspace_bytes(B, Hq, Hkv, S, d, dtype=torch.bfloat16):
 
 def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=None, events=None):
     """Backward: gradients of sum(o * dout) -> (dq, dk, dv).  ``events``: an
-    optional sequence of 5 hipEvent_t handles (ints) recorded around the four
+    optional sequence of 4 hipEvent_t handles (ints) recorded around the three
     kernels (see sepattn_bwd_profiled)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]

@@ -29,7 +29,8 @@ bool index_ok(const sepattn_index* idx, int B, int S) {
 }
 
 int check_attn(int B, int Hq, int Hkv, int S, int d, int dtype, float scale) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0 || !(isfinite(scale))) return SEPATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0 || !(isfinite(scale) && scale > 0.f))
+    return SEPATTN_EINVAL;
   if (dtype != SEPATTN_F32 && dtype != SEPATTN_BF16) return SEPATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return SEPATTN_EUNSUPPORTED;
   return SEPATTN_OK;
@@ -187,7 +188,7 @@ static int decode_common(const sepcache* cache, const void* q, int Hq, const flo
                          void* stream, hipEvent_t* ev) {
   int st = check_cache(cache);
   if (st != SEPATTN_OK) return st;
-  if (!q || !rope_cos || !rope_sin || !o || Hq < 1 || Hq % cache->Hkv != 0 || !isfinite(scale))
+  if (!q || !rope_cos || !rope_sin || !o || Hq < 1 || Hq % cache->Hkv != 0 || !(isfinite(scale) && scale > 0.f))
     return SEPATTN_EINVAL;
   const int G = Hq / cache->Hkv;
   if (G > kMaxDecodeGroup || (G & (G - 1)) != 0) return SEPATTN_EUNSUPPORTED;

@@ -8,36 +8,51 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q,
 // dK/dV summed over the query heads of each kv group.
 //
-// Kernels, in launch order:
-//   pre   : D_i = rowsum(dO * O)
-//   dkdv<anchor>: key-major over gathered anchor tiles (128 anchors per
-//           workgroup), the query tiles split into a few chunks; each (anchor
-//           tile, chunk) stores its fp32 partial in its own slot (plain
-//           stores, zeros when the chunk sees none of the anchors)
-//   dkdv<band>  : key-major over 128-key tiles of the local band; each
-//           workgroup owns its rows, adds the chunk partials of rows that are
-//           anchors, scales and stores dK/dV in the input type
-//   dq    : query-major, same schedule as the forward
+// Launches:
+//   pre      : D_i = rowsum(dO * O)
+//   main     : one grid of three kinds of independent work items, so the long
+//              anchor reductions run beside the short items instead of alone:
+//     anchor dK/dV -- key-major over gathered anchor tiles (128 anchors per
+//              workgroup); the query tiles are split into chunks and each
+//              (anchor tile, chunk) stores its fp32 partial in its own slot;
+//     dQ       -- query-major over the forward's schedule;
+//     band dK/dV -- key-major over 128-key tiles of the local band; a
+//              workgroup owns its rows: rows that are not anchors seen through
+//              the anchor path are scaled and stored in the input type, the
+//              others store an fp32 partial in one more slot;
+//   finalize : rows that are anchors sum their slots and are stored.
 //
 // Key-major formulation: S = Q K^T with queries on the MFMA M axis and the
 // workgroup's keys on the N axis (lanes), so dV^T = dO^T P and dK^T = Q^T dS
-// take P and dS straight from the score registers; Q and dO are staged in LDS
-// both row-major and transposed.  Query-major (dq): S^T = K Q^T as in the
-// forward, dP^T = V dO^T, dQ^T = K^T dS^T with K transposed in LDS.
+// take P and dS straight from the score registers; the transposed operands
+// dO^T and Q^T are read from the row-major LDS tiles with the transpose read.
+// Query-major (dQ): S^T = K Q^T as in the forward, dP^T = V dO^T,
+// dQ^T = K^T dS^T.
 #include "internal.hpp"
 #include "tile.hpp"
 
 namespace sepattn {
 
 constexpr int kBwdThreads = 256;
+constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
 
-// Workgroups per CU the register budget targets: the d=128 and fp32 backward
-// kernels keep more operands resident than fit two waves per SIMD.
+// Workgroups per CU the register budget targets, and how many tiles ahead
+// global loads are issued: the d=128 and fp32 kernels keep more operands
+// resident than fit two waves per SIMD with two tiles in flight.
 template <typename T, int D>
 constexpr int bwd_occupancy() {
   return (sizeof(T) == 2 && D == 64) ? 2 : 1;
 }
-constexpr int kKeysPerWG = 128;   // 4 waves x 32 keys
+#ifndef SEPATTN_DKDV_PREFETCH
+#define SEPATTN_DKDV_PREFETCH 1
+#endif
+#ifndef SEPATTN_DQ_PREFETCH
+#define SEPATTN_DQ_PREFETCH 1
+#endif
+template <typename T, int D, bool KEY_MAJOR>
+constexpr int bwd_prefetch() {
+  return (sizeof(T) == 2 && D == 64) ? (KEY_MAJOR ? SEPATTN_DKDV_PREFETCH : SEPATTN_DQ_PREFETCH) : 1;
+}
 
 struct BwdArgs {
   const void* q;
@@ -50,7 +65,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* Dvec;  // [B,Hq,S]
-  float* dKa;   // [nchunk,B,Hkv,S,D] anchor partials, by chunk and anchor index
+  float* dKa;   // [nchunk+1,B,Hkv,S,D] fp32 partials by slot and anchor index
   float* dVa;
   const uint8_t* is_sep;
   const int32_t* sep_prefix;
@@ -58,6 +73,8 @@ struct BwdArgs {
   const int32_t* qtile;
   int B, Hq, Hkv, S, a, n, QT;
   int nchunk, chunk_tiles;  // anchor work split: nchunk chunks of chunk_tiles query tiles
+  int units;                // ceil(S / 128) key units per (sequence, kv head)
+  int n_anchor_items, n_dq_items, n_band_items;
   float scale;
   float scale_log2;
 };
@@ -74,6 +91,17 @@ static void anchor_split(int B, int Hkv, int S, int QT, int* nchunk, int* chunk_
   const int ct = (int)((QT + n - 1) / n);
   *chunk_tiles = ct;
   *nchunk = (QT + ct - 1) / ct;
+}
+
+// Anchor index of key row `krow` if it is an anchor that some query sees
+// through the anchor path (index below the last query tile's anchor count),
+// else -1.
+__device__ __forceinline__ int anchor_slot(const BwdArgs& p, int b, int krow, bool key_sep, int n_last) {
+  const int n_init = p.a < p.S ? p.a : p.S;
+  int ai = -1;
+  if (krow < n_init) ai = krow;
+  else if (key_sep) ai = n_init + p.sep_prefix[(size_t)b * (p.S + 1) + krow];
+  return (ai >= 0 && ai < n_last) ? ai : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -108,10 +136,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// key-major dK/dV
+// key-major dK/dV of one key unit (128 keys) against a range of query tiles
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool ANCHOR>
-__global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv_kernel(BwdArgs p) {
+__device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk, T* Qs, T* dOs,
+                                          float* lse_s, float* dd_s) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kBwdThreads> Regs;
@@ -121,42 +150,29 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
   constexpr int NF = D / KSTEP;    // K/V fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of dK^T / dV^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps over one 32-query block
-
-  __shared__ __attribute__((aligned(16))) T Qs[2][G::ELEMS];   // 64 query rows, row-major
-  __shared__ __attribute__((aligned(16))) T dOs[2][G::ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][kKTile];
-  __shared__ __attribute__((aligned(16))) float dd_s[2][kKTile];
+  constexpr int PF = bwd_prefetch<T, D, true>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hh = lane >> 5;
   const int kc = lane & 31;
-
-  const int bg = blockIdx.y;
-  const int b = bg / p.Hkv;
-  const int g = bg - b * p.Hkv;
   const int grp = p.Hq / p.Hkv;
   const int32_t* qt = p.qtile + (size_t)b * p.QT * kQF;
   const int n_last = qt[(p.QT - 1) * kQF + 1];
 
-  int unit, qi_begin, qi_end;  // key unit and query-tile range [qi_begin, qi_end)
-  int chunk = 0;
+  int qi_begin, qi_end;  // query-tile range [qi_begin, qi_end)
   if constexpr (ANCHOR) {
-    unit = blockIdx.x / p.nchunk;
-    chunk = blockIdx.x - unit * p.nchunk;
-    if (unit * kKeysPerWG >= n_last) return;  // no query sees these anchors; never read
-    // first query tile whose anchor count exceeds this unit's first anchor
-    int lo_t = 0, hi_t = p.QT - 1;
-    while (lo_t < hi_t) {
-      const int mid = (lo_t + hi_t) >> 1;
-      if (qt[mid * kQF + 1] > unit * kKeysPerWG) hi_t = mid;
-      else lo_t = mid + 1;
-    }
-    qi_begin = max(lo_t, chunk * p.chunk_tiles);
+    // Query tile qi sees anchor number j iff anchor_pos[j] < lo(qi) =
+    // max(0, 128 qi - n + 1): the first tile that sees this unit's first
+    // anchor (position p0) is (p0 + n - 1) / 128 + 1.
+    const int a0 = unit * kKeysPerWG;
+    const int p0 = a0 < p.S ? p.anchor_pos[(size_t)b * p.S + a0] : -1;
+    const int first = p0 >= 0 ? (p0 + p.n - 1) / kQTile + 1 : p.QT;
+    if (first >= p.QT) return;  // no query sees these anchors; never read
+    qi_begin = max(first, chunk * p.chunk_tiles);
     qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);  // may be empty: the slot is then zero-filled
   } else {
-    unit = blockIdx.x;
     const int k0 = unit * kKeysPerWG;
     const int k1 = min(k0 + kKeysPerWG - 1, p.S - 1);
     qi_begin = k0 / kQTile;
@@ -168,10 +184,13 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
   // this lane's key
   const int kidx = unit * kKeysPerWG + 32 * w + kc;  // key row (band) or anchor index (anchor)
   int krow;
-  if constexpr (ANCHOR) krow = kidx < n_last ? p.anchor_pos[(size_t)b * p.S + kidx] : -1;
+  // (anchor-list entries past the anchor count are -1; anchors at or past
+  // n_last get zero weight from the visibility test and their slots are
+  // never read)
+  if constexpr (ANCHOR) krow = kidx < p.S ? p.anchor_pos[(size_t)b * p.S + kidx] : -1;
   else krow = kidx < p.S ? kidx : -1;
   const bool key_sep = (!ANCHOR && krow >= 0) ? (p.is_sep[(size_t)b * p.S + krow] != 0) : false;
-  // band: rows that see this key through the window or because it is an anchor-type key
+  // band: last row that sees this key (all later rows for initial / separator keys)
   const int q_hi = (krow < p.a || key_sep) ? p.S - 1 : min(p.S - 1, krow + p.n - 1);
 
   const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
@@ -182,10 +201,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
     const int r = it % (2 * n_q);
     return (qi_begin + (r >> 1)) * kQTile + (r & 1) * kKTile;
   };
-
-  Regs rq, ro;
-  float pf_lse = 0.f, pf_d = 0.f;
-  auto issue = [&](int it) {
+  auto issue = [&](int it, Regs& rq, Regs& ro, float& pl, float& pd) {
     const int h = it_head(it);
     const int r0 = it_row0(it);
     int rows[Regs::NU];
@@ -195,11 +211,15 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
     if (tid < kKTile) {
       const int r = r0 + tid;
       const size_t o = ((size_t)b * p.Hq + h) * p.S + r;
-      pf_lse = r < p.S ? p.lse[o] * 1.4426950408889634f : 0.f;
-      pf_d = r < p.S ? p.Dvec[o] : 0.f;
+      pl = r < p.S ? p.lse[o] * 1.4426950408889634f : 0.f;
+      pd = r < p.S ? p.Dvec[o] : 0.f;
     }
   };
-  if (n_it > 0) issue(0);
+
+  Regs rqA, roA, rqB, roB;
+  float plA = 0.f, pdA = 0.f, plB = 0.f, pdB = 0.f;
+  if (n_it > 0) issue(0, rqA, roA, plA, pdA);
+  if (PF == 2 && n_it > 1) issue(1, rqB, roB, plB, pdB);
 
   frag kf[NF], vf[NF];
 #pragma unroll
@@ -220,20 +240,24 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
     dv[db] = f32x16{};
   }
 
-  for (int it = 0; it < n_it; ++it) {
+  auto step = [&](int it, Regs& rq, Regs& ro, float& pl, float& pd) {
     const int buf = it & 1;
-    rq.store(Qs[buf], tid);
-    ro.store(dOs[buf], tid);
+    T* Qb = Qs + buf * G::ELEMS;
+    T* dOb = dOs + buf * G::ELEMS;
+    float* lb = lse_s + buf * kKTile;
+    float* db_ = dd_s + buf * kKTile;
+    rq.store(Qb, tid);
+    ro.store(dOb, tid);
     if (tid < kKTile) {
-      lse_s[buf][tid] = pf_lse;
-      dd_s[buf][tid] = pf_d;
+      lb[tid] = pl;
+      db_[tid] = pd;
     }
-    __syncthreads();
+    __syncthreads();  // tile `it` visible; every wave is done with tile it-1's buffer
     const int r0 = it_row0(it);
     const int qi = r0 / kQTile;
-    if (it + 1 < n_it) issue(it + 1);
+    if (it + PF < n_it) issue(it + PF, rq, ro, pl, pd);
 
-    // query-row range [ql, qh] of the rows r0 .. r0+63 that see this lane's key
+    // query-row range [ql, qh] of the rows that see this lane's key
     int ql, qh;
     if constexpr (ANCHOR) {
       const bool seen = krow >= 0 && kidx < qt[qi * kQF + 1];
@@ -244,120 +268,130 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dkdv
       ql = in_band ? krow : 1;
       qh = in_band ? q_hi : 0;
     }
-    const T* Q = Qs[buf];
-    const T* dO = dOs[buf];
+    // every row of this 64-row chunk sees every key of the wave: skip the tests
+    const bool full = __all(ql <= r0 && qh >= r0 + kKTile - 1);
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        frag qq[NF], oo[NF];  // operands first, then the MFMAs back to back
 #pragma unroll
-      for (int c = 0; c < NF; ++c) {
-        sacc = Tr::mfma(read_x<T, D>(Q, mb, c, lane), kf[c], sacc);
-        pacc = Tr::mfma(read_x<T, D>(dO, mb, c, lane), vf[c], pacc);
+        for (int c = 0; c < NF; ++c) {
+          qq[c] = read_x<T, D>(Qb, mb, c, lane);
+          oo[c] = read_x<T, D>(dOb, mb, c, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < NF; ++c) {
+          sacc = Tr::mfma(qq[c], kf[c], sacc);
+          pacc = Tr::mfma(oo[c], vf[c], pacc);
+        }
       }
       // P and dS; rows are queries r0 + 32mb + acc_row(i), column is this lane's key
+      // (rows past S were loaded as zeros with zero LSE and D, so they add nothing)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int rl0 = 32 * mb + 8 * i4 + 4 * hh;
-        const f32x4 l4 = *(const f32x4*)&lse_s[buf][rl0];
-        const f32x4 d4 = *(const f32x4*)&dd_s[buf][rl0];
+        const f32x4 l4 = *(const f32x4*)&lb[rl0];
+        const f32x4 d4 = *(const f32x4*)&db_[rl0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
-          const int q = r0 + rl0 + e;
-          const bool vis = q >= ql && q <= qh;
-          const float pv = vis ? fast_exp2(sacc[i] * p.scale_log2 - l4[e]) : 0.f;
+          const float pv = fast_exp2(__builtin_fmaf(sacc[i], p.scale_log2, -l4[e]));
           sacc[i] = pv;
           pacc[i] = pv * (pacc[i] - d4[e]);
         }
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS
+      if (!full) {  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = r0 + 32 * mb + acc_row(i, hh);
+          const bool on = q >= ql && q <= qh;
+          sacc[i] = on ? sacc[i] : 0.f;
+          pacc[i] = on ? pacc[i] : 0.f;
+        }
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS (per step: operands first, then MFMAs)
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) {
+        frag ot[NDB], qt_[NDB];
+#pragma unroll
+        for (int dbk = 0; dbk < NDB; ++dbk) {
+          ot[dbk] = read_xt<T, D>(dOb, mb, sl, 32 * dbk, lane);
+          qt_[dbk] = read_xt<T, D>(Qb, mb, sl, 32 * dbk, lane);
+        }
         const frag pf = acc_frag<T>(sacc, sl);
         const frag sf = acc_frag<T>(pacc, sl);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = Tr::mfma(read_xt<T, D>(dO, mb, sl, 32 * db, lane), pf, dv[db]);
-          dk[db] = Tr::mfma(read_xt<T, D>(Q, mb, sl, 32 * db, lane), sf, dk[db]);
+        for (int dbk = 0; dbk < NDB; ++dbk) {
+          dv[dbk] = Tr::mfma(ot[dbk], pf, dv[dbk]);
+          dk[dbk] = Tr::mfma(qt_[dbk], sf, dk[dbk]);
         }
       }
     }
+  };
+
+  if constexpr (PF == 2) {
+    for (int it = 0; it < n_it; it += 2) {
+      step(it, rqA, roA, plA, pdA);
+      if (it + 1 < n_it) step(it + 1, rqB, roB, plB, pdB);
+    }
+  } else {
+    for (int it = 0; it < n_it; ++it) step(it, rqA, roA, plA, pdA);
   }
 
   // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i)
+  if (krow < 0) return;
+  float* ka = nullptr;
+  float* va = nullptr;
+  T* dkg = nullptr;
+  T* dvg = nullptr;
   if constexpr (ANCHOR) {
-    if (krow >= 0) {
-      const size_t slot = (((size_t)chunk * p.B + b) * p.Hkv + g) * p.S + kidx;
-      float* ka = p.dKa + slot * D;
-      float* va = p.dVa + slot * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = 32 * db + 8 * r4 + 4 * hh;
-          *(f32x4*)(ka + d0) = f32x4{dk[db][4 * r4] * p.scale, dk[db][4 * r4 + 1] * p.scale,
-                                     dk[db][4 * r4 + 2] * p.scale, dk[db][4 * r4 + 3] * p.scale};
-          *(f32x4*)(va + d0) = f32x4{dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
-        }
-    }
+    const size_t off = (((size_t)chunk * p.B + b) * p.Hkv + g) * p.S + kidx;
+    ka = p.dKa + off * D;
+    va = p.dVa + off * D;
   } else {
-    if (krow >= 0) {
-      // is this key also an anchor that some query sees through the anchor path?
-      const int n_init = p.a < p.S ? p.a : p.S;
-      int ai = -1;
-      if (krow < n_init) ai = krow;
-      else if (key_sep) ai = n_init + p.sep_prefix[(size_t)b * (p.S + 1) + krow];
-      const bool add = ai >= 0 && ai < n_last;
-      const size_t cstride = (size_t)p.B * p.Hkv * p.S * D;  // between chunk slots
-      const float* ka = p.dKa + (((size_t)b * p.Hkv + g) * p.S + (add ? ai : 0)) * D;
-      const float* va = p.dVa + (((size_t)b * p.Hkv + g) * p.S + (add ? ai : 0)) * D;
-      T* dkg = (T*)p.dk + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
-      T* dvg = (T*)p.dv + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = 32 * db + 8 * r4 + 4 * hh;
-          float kv4[4], vv4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv4[e] = dk[db][4 * r4 + e] * p.scale;
-            vv4[e] = dv[db][4 * r4 + e];
-          }
-          if (add) {
-            for (int c = 0; c < p.nchunk; ++c) {
-              const f32x4 ak = *(const f32x4*)(ka + c * cstride + d0);
-              const f32x4 av = *(const f32x4*)(va + c * cstride + d0);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                kv4[e] += ak[e];
-                vv4[e] += av[e];
-              }
-            }
-          }
-          if constexpr (EPL == 8) {
-            u32x2 pk, pv2;
-            pk[0] = pack_bf16x2(kv4[0], kv4[1]);
-            pk[1] = pack_bf16x2(kv4[2], kv4[3]);
-            pv2[0] = pack_bf16x2(vv4[0], vv4[1]);
-            pv2[1] = pack_bf16x2(vv4[2], vv4[3]);
-            *(u32x2*)(dkg + d0) = pk;
-            *(u32x2*)(dvg + d0) = pv2;
-          } else {
-            *(f32x4*)(dkg + d0) = f32x4{kv4[0], kv4[1], kv4[2], kv4[3]};
-            *(f32x4*)(dvg + d0) = f32x4{vv4[0], vv4[1], vv4[2], vv4[3]};
-          }
-        }
+    const int ai = anchor_slot(p, b, krow, key_sep, n_last);
+    if (ai >= 0) {
+      const size_t off = (((size_t)p.nchunk * p.B + b) * p.Hkv + g) * p.S + ai;
+      ka = p.dKa + off * D;
+      va = p.dVa + off * D;
+    } else {
+      dkg = (T*)p.dk + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
+      dvg = (T*)p.dv + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
     }
   }
+#pragma unroll
+  for (int dbk = 0; dbk < NDB; ++dbk)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * dbk + 8 * r4 + 4 * hh;
+      const f32x4 kv4 = {dk[dbk][4 * r4] * p.scale, dk[dbk][4 * r4 + 1] * p.scale, dk[dbk][4 * r4 + 2] * p.scale,
+                         dk[dbk][4 * r4 + 3] * p.scale};
+      const f32x4 vv4 = {dv[dbk][4 * r4], dv[dbk][4 * r4 + 1], dv[dbk][4 * r4 + 2], dv[dbk][4 * r4 + 3]};
+      if (ka) {
+        *(f32x4*)(ka + d0) = kv4;
+        *(f32x4*)(va + d0) = vv4;
+      } else if constexpr (EPL == 8) {
+        u32x2 pk, pv2;
+        pk[0] = pack_bf16x2(kv4[0], kv4[1]);
+        pk[1] = pack_bf16x2(kv4[2], kv4[3]);
+        pv2[0] = pack_bf16x2(vv4[0], vv4[1]);
+        pv2[1] = pack_bf16x2(vv4[2], vv4[3]);
+        *(u32x2*)(dkg + d0) = pk;
+        *(u32x2*)(dvg + d0) = pv2;
+      } else {
+        *(f32x4*)(dkg + d0) = kv4;
+        *(f32x4*)(dvg + d0) = vv4;
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// query-major dQ over the forward's schedule
+// query-major dQ of one query tile over the forward's schedule
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dq_kernel(BwdArgs p) {
+__device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, T* Ks, T* Vs) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kBwdThreads> Regs;
@@ -367,26 +401,23 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dq_k
   constexpr int NQF = D / KSTEP;
   constexpr int NDB = D / 32;
   constexpr int SPB = 32 / KSTEP;
-
-  __shared__ __attribute__((aligned(16))) T Ks[2][G::ELEMS];
-  __shared__ __attribute__((aligned(16))) T Vs[2][G::ELEMS];
+  constexpr int PF = bwd_prefetch<T, D, false>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hh = lane >> 5;
   const int qc = lane & 31;
-
-  const int qi = p.QT - 1 - (int)blockIdx.y;
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
   const int g = h / (p.Hq / p.Hkv);
 
-  const int32_t* qt = p.qtile + ((size_t)b * p.QT + qi) * kQF;
-  const int lo = qt[0], n_anchor = qt[1], kb = qt[2], ke = qt[3], q0 = qt[6];
+  // band tiles first (rows follow from q0 and n), gathered anchor tiles last
+  const int q0 = qi * kQTile;
+  const int lo = max(0, q0 - p.n + 1);
+  const int kb = lo / kKTile, ke = min(q0 + kQTile - 1, p.S - 1) / kKTile;
+  const int n_band = ke - kb + 1;
+  const int n_anchor = p.qtile[((size_t)b * p.QT + qi) * kQF + 1];
   const int n_at = (n_anchor + kKTile - 1) / kKTile;
-  const int n_tiles = n_at + ke - kb + 1;
+  const int n_tiles = n_band + n_at;
 
   const int iq = q0 + 32 * w + qc;
   const bool q_ok = iq < p.S;
@@ -400,30 +431,33 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dq_k
 
   auto src_of = [&](int t) {
     RowSrc r;
-    if (t < n_at) {
+    if (t >= n_band) {
       r.anchor = anc;
-      r.base = t * kKTile;
+      r.base = (t - n_band) * kKTile;
       r.limit = n_anchor;
     } else {
       r.anchor = nullptr;
-      r.base = (kb + t - n_at) * kKTile;
+      r.base = (kb + t) * kKTile;
       r.limit = p.S;
     }
     return r;
   };
-  auto sep_flag = [&](int t) -> int {
-    if (t < n_at) return 0;
-    const int j = (kb + t - n_at) * kKTile + lane;
-    return j < p.S ? (int)sepf[j] : 0;
+  auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
+    int rows[Regs::NU];
+    Regs::rows(rows, src_of(t), tid);
+    rk.issue(Kg, rows, tid);
+    rv.issue(Vg, rows, tid);
+    sflag = 0;
+    if (t < n_band) {
+      const int j = (kb + t) * kKTile + lane;
+      sflag = j < p.S ? (int)sepf[j] : 0;
+    }
   };
 
-  Regs rk, rv;
-  int rows[Regs::NU];
-  Regs::rows(rows, src_of(0), tid);
-  rk.issue(Kg, rows, tid);
-  rv.issue(Vg, rows, tid);
-  int sflag = sep_flag(0);
-  if (n_tiles > 1) Regs::rows(rows, src_of(1), tid);
+  Regs rkA, rvA, rkB, rvB;
+  int sA = 0, sB = 0;
+  issue(0, rkA, rvA, sA);
+  if (PF == 2 && n_tiles > 1) issue(1, rkB, rvB, sB);
 
   frag qf[NQF], of[NQF];
 #pragma unroll
@@ -446,63 +480,87 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dq_k
   const int wrow0 = q0 + 32 * w;
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
-  for (int t = 0; t < n_tiles; ++t) {
+  auto step = [&](int t, Regs& rk, Regs& rv, int& sflag) {
     const int buf = t & 1;
-    rk.store(Ks[buf], tid);
-    rv.store(Vs[buf], tid);
+    T* K = Ks + buf * G::ELEMS;
+    T* V = Vs + buf * G::ELEMS;
+    rk.store(K, tid);
+    rv.store(V, tid);
     const uint64_t sepbits = __ballot(sflag != 0);
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      rk.issue(Kg, rows, tid);
-      rv.issue(Vg, rows, tid);
-      sflag = sep_flag(t + 1);
-      if (t + 2 < n_tiles) Regs::rows(rows, src_of(t + 2), tid);
-    }
-    const T* K = Ks[buf];
-    const T* V = Vs[buf];
+    if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
 
-    const bool anchor_tile = t < n_at;
+    const bool anchor_tile = t >= n_band;
     bool full;
     uint64_t vis;
     if (anchor_tile) {
-      const int nv = n_anchor - t * kKTile;
+      const int nv = n_anchor - (t - n_band) * kKTile;
       full = nv >= kKTile;
       vis = bit_range(0, nv - 1);
     } else {
-      const int c0 = (kb + t - n_at) * kKTile;
+      const int c0 = (kb + t) * kKTile;
       full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
       vis = band_visible(iq, c0, lo, p.S, p.a, p.n, sepbits);
     }
     vis >>= 4 * hh;
-    full = full && q_ok;
 
+    // rows past S have zero Q, dO, LSE and D, so their dS is zero unmasked
     f32x16 ds[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        frag kk[NQF], vv[NQF];  // operands first, then the MFMAs back to back
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        sacc = Tr::mfma(read_x<T, D>(K, k2, c, lane), qf[c], sacc);
-        pacc = Tr::mfma(read_x<T, D>(V, k2, c, lane), of[c], pacc);
+        for (int c = 0; c < NQF; ++c) {
+          kk[c] = read_x<T, D>(K, k2, c, lane);
+          vv[c] = read_x<T, D>(V, k2, c, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+          sacc = Tr::mfma(kk[c], qf[c], sacc);
+          pacc = Tr::mfma(vv[c], of[c], pacc);
+        }
       }
-      const uint32_t vw = q_ok ? (uint32_t)(vis >> (32 * k2)) : 0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool on = full || ((vw >> (((i >> 2) << 3) + (i & 3))) & 1u);
-        const float pv = on ? fast_exp2(sacc[i] * p.scale_log2 - lse2) : 0.f;
+        const float pv = fast_exp2(__builtin_fmaf(sacc[i], p.scale_log2, -lse2));
         ds[k2][i] = pv * (pacc[i] - Di);
+      }
+      if (!full) {  // wave-uniform
+        const uint32_t vw = (uint32_t)(vis >> (32 * k2));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool on = (vw >> (((i >> 2) << 3) + (i & 3))) & 1u;
+          ds[k2][i] = on ? ds[k2][i] : 0.f;
+        }
       }
     }
 
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T, one 32-key half at a time with its K^T operands read first
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int k2 = 0; k2 < 2; ++k2) {
+      frag kt[SPB][NDB];
+#pragma unroll
+      for (int sl = 0; sl < SPB; ++sl)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) kt[sl][db] = read_xt<T, D>(K, k2, sl, 32 * db, lane);
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) {
         const frag sf = acc_frag<T>(ds[k2], sl);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(read_xt<T, D>(K, k2, sl, 32 * db, lane), sf, dq[db]);
+        for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[sl][db], sf, dq[db]);
       }
+    }
+  };
+
+  if constexpr (PF == 2) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, rkA, rvA, sA);
+      if (t + 1 < n_tiles) step(t + 1, rkB, rvB, sB);
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) step(t, rkA, rvA, sA);
   }
 
   if (q_ok) {
@@ -529,6 +587,76 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_dq_k
 }
 
 // ---------------------------------------------------------------------------
+// main: anchor dK/dV items, then dQ items (heaviest query tiles first), then
+// band dK/dV items, in one 1-D grid
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main_kernel(BwdArgs p) {
+  typedef TileGeom<T, D> G;
+  __shared__ __attribute__((aligned(16))) T smA[2 * G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smB[2 * G::ELEMS];
+  __shared__ __attribute__((aligned(16))) float smL[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) float smD[2 * kKTile];
+
+  int x = blockIdx.x;
+  const int BG = p.B * p.Hkv;
+  if (x < p.n_anchor_items) {
+    // unit-major so the few active anchor units come first
+    const int per_unit = BG * p.nchunk;
+    const int unit = x / per_unit;
+    const int r = x - unit * per_unit;
+    const int bg = r / p.nchunk;
+    const int chunk = r - bg * p.nchunk;
+    dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smL, smD);
+    return;
+  }
+  x -= p.n_anchor_items;
+  if (x < p.n_dq_items) {
+    const int BH = p.B * p.Hq;
+    const int qi = p.QT - 1 - x / BH;
+    const int bh = x % BH;
+    dq_item<T, D>(p, bh / p.Hq, bh % p.Hq, qi, smA, smB);
+    return;
+  }
+  // band items: the units of one (sequence, kv head) share query tiles, so
+  // keep each (sequence, kv head) on one XCD's L2
+  const int li = xcd_local_index(blockIdx.x, p.n_anchor_items + p.n_dq_items, p.n_band_items);
+  const int bg = li / p.units;
+  const int unit = li - bg * p.units;
+  dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, smA, smB, smL, smD);
+}
+
+// ---------------------------------------------------------------------------
+// finalize: anchor rows = sum of their partial slots, stored in the input type
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdArgs p) {
+  constexpr int TPR = D / 4;  // threads per row, 4 elements each
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv;
+  const int n_last = p.qtile[((size_t)b * p.QT + p.QT - 1) * kQF + 1];
+  const int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (ai >= n_last) return;
+  const int c4 = (threadIdx.x % TPR) * 4;
+  const size_t cstride = (size_t)p.B * p.Hkv * p.S * D;
+  const size_t off = ((size_t)bg * p.S + ai) * D + c4;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c <= p.nchunk; ++c) {
+    sk += *(const f32x4*)(p.dKa + c * cstride + off);
+    sv += *(const f32x4*)(p.dVa + c * cstride + off);
+  }
+  const int krow = p.anchor_pos[(size_t)b * p.S + ai];
+  const size_t o = ((size_t)bg * p.S + krow) * D + c4;
+  if constexpr (sizeof(T) == 2) {
+    *(u32x2*)((uint16_t*)p.dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+    *(u32x2*)((uint16_t*)p.dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+  } else {
+    *(f32x4*)((float*)p.dk + o) = sk;
+    *(f32x4*)((float*)p.dv + o) = sv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -536,7 +664,7 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   const int QT = (S + kQTile - 1) / kQTile;
   int nchunk, ct;
   anchor_split(B, Hkv, S, QT, &nchunk, &ct);
-  return a256((size_t)B * Hq * S * 4) + 2 * a256((size_t)nchunk * B * Hkv * S * d * 4);
+  return a256((size_t)B * Hq * S * 4) + 2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
 }
 
 template <typename T, int D>
@@ -544,22 +672,21 @@ static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   constexpr int TPR = D / Traits<T>::VEC;
   const size_t rows = (size_t)a.B * a.Hq * a.S;
   const int pre_blocks = (int)((rows + (256 / TPR) - 1) / (256 / TPR));
-  const int units = (a.S + kKeysPerWG - 1) / kKeysPerWG;
+  const int main_blocks = a.n_anchor_items + a.n_dq_items + a.n_band_items;
+  const int fin_rows_per_block = 256 / (D / 4);
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_blocks), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(units * a.nchunk, a.B * a.Hkv), dim3(kBwdThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(units, a.B * a.Hkv), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
+                                                       a.B * a.Hkv),
+                     dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.B * a.Hq, a.QT), dim3(kBwdThreads), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -582,7 +709,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.QT = (sh.S + kQTile - 1) / kQTile;
   anchor_split(sh.B, sh.Hkv, sh.S, a.QT, &a.nchunk, &a.chunk_tiles);
   a.dKa = (float*)w;
-  w += a256((size_t)a.nchunk * sh.B * sh.Hkv * sh.S * sh.d * 4);
+  w += a256((size_t)(a.nchunk + 1) * sh.B * sh.Hkv * sh.S * sh.d * 4);
   a.dVa = (float*)w;
   a.is_sep = idx.is_sep;
   a.sep_prefix = idx.sep_prefix;
@@ -594,7 +721,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.S = sh.S;
   a.a = idx.a;
   a.n = idx.n;
-  a.QT = (sh.S + kQTile - 1) / kQTile;
+  a.units = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
+  a.n_anchor_items = a.units * sh.B * sh.Hkv * a.nchunk;
+  a.n_dq_items = sh.B * sh.Hq * a.QT;
+  a.n_band_items = a.units * sh.B * sh.Hkv;
   a.scale = sh.scale;
   a.scale_log2 = sh.scale * 1.4426950408889634f;
   if (sh.dtype == SEPATTN_BF16) {

@@ -49,7 +49,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Swap with the lane 32 apart (the other half of the wave).
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Reductions over the lane pair (l, l ^ 32) in registers: v_permlane32_swap
+// of (x, x) yields [x_lo, x_lo] and [x_hi, x_hi] (lower / upper 32 lanes).
+__device__ __forceinline__ float pair_max(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Work-item order that keeps contiguous runs of logical items on one XCD:
+// workgroups are dealt round-robin to the 8 XCDs by launch index, so item
+// `g - base` of a segment [base, base + n) is renumbered so that each XCD
+// receives one contiguous range of logical indices.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_local_index(int g, int base, int n) {
+  constexpr int kXcd = 8;
+  const int c = g % kXcd;                         // this workgroup's XCD
+  const int first = ((c - base) % kXcd + kXcd) % kXcd;  // first segment offset on XCD c
+  int before = 0;                                 // items of the segment on XCDs < c
+  for (int x = 0; x < c; ++x) {
+    const int f = ((x - base) % kXcd + kXcd) % kXcd;
+    before += f < n ? (n - f + kXcd - 1) / kXcd : 0;
+  }
+  return before + ((g - base) - first) / kXcd;
+}
 
 }  // namespace sepattn

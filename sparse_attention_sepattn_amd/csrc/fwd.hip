@@ -1,8 +1,8 @@
 // Forward of SepLLM separator-sparse attention: block-sparse flash attention
-// over the kept tiles of each 128-row query tile -- ceil(n_anchor/64) tiles of
-// gathered anchors (initial tokens and separators below the window, visible to
-// every row of the tile, so unmasked) and the key tiles kt_begin..kt_end of
-// the local band (masked element-wise).  Online softmax in the base-2 domain,
+// over the kept tiles of each 128-row query tile -- the key tiles
+// kt_begin..kt_end of the local band (masked element-wise), then
+// ceil(n_anchor/64) tiles of gathered anchors (initial tokens and separators
+// below the window, visible to every row of the tile, so unmasked).  Online softmax in the base-2 domain,
 // fp32 accumulation, P rounded to the input type for the second product.
 //
 // Mask: SepLLM summary on atlas.scime.ai, "Approach".  Output O = M(A, V, M_b)
@@ -27,6 +27,11 @@ struct FwdArgs {
 };
 
 constexpr int kFwdThreads = 256;
+// Lazy rescaling threshold (base-2 units): probabilities stay below 2^8.
+constexpr float kLazy = 8.f;
+#ifndef SEPATTN_FWD_PREFETCH
+#define SEPATTN_FWD_PREFETCH 2
+#endif
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kernel(FwdArgs p) {
@@ -39,6 +44,7 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   constexpr int NQF = D / KSTEP;   // Q fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of O^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps per 32-key block
+  constexpr int PF = (sizeof(T) == 2 && D == 64) ? SEPATTN_FWD_PREFETCH : 1;  // tiles in flight
 
   __shared__ __attribute__((aligned(16))) T Ks[2][G::ELEMS];
   __shared__ __attribute__((aligned(16))) T Vs[2][G::ELEMS];
@@ -56,10 +62,15 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   const int h = bh - b * p.Hq;
   const int g = h / (p.Hq / p.Hkv);
 
-  const int32_t* qt = p.qtile + ((size_t)b * p.QT + qi) * kQF;
-  const int lo = qt[0], n_anchor = qt[1], kb = qt[2], ke = qt[3], q0 = qt[6];
+  // Band tiles first (their rows follow from q0 and n), gathered anchor tiles
+  // last, so the first loads do not wait for the index.
+  const int q0 = qi * kQTile;
+  const int lo = max(0, q0 - p.n + 1);
+  const int kb = lo / kKTile, ke = min(q0 + kQTile - 1, p.S - 1) / kKTile;
+  const int n_band = ke - kb + 1;
+  const int n_anchor = p.qtile[((size_t)b * p.QT + qi) * kQF + 1];
   const int n_at = (n_anchor + kKTile - 1) / kKTile;
-  const int n_tiles = n_at + ke - kb + 1;
+  const int n_tiles = n_band + n_at;
 
   const int iq = q0 + 32 * w + qc;  // this lane's query row
   const bool q_ok = iq < p.S;
@@ -71,31 +82,35 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
 
   auto src_of = [&](int t) {
     RowSrc r;
-    if (t < n_at) {
+    if (t >= n_band) {
       r.anchor = anc;
-      r.base = t * kKTile;
+      r.base = (t - n_band) * kKTile;
       r.limit = n_anchor;
     } else {
       r.anchor = nullptr;
-      r.base = (kb + t - n_at) * kKTile;
+      r.base = (kb + t) * kKTile;
       r.limit = p.S;
     }
     return r;
   };
   auto sep_flag = [&](int t) -> int {
-    if (t < n_at) return 0;
-    const int j = (kb + t - n_at) * kKTile + lane;
+    if (t >= n_band) return 0;
+    const int j = (kb + t) * kKTile + lane;
     return j < p.S ? (int)sepf[j] : 0;
   };
 
-  // prologue: tile 0 in flight, rows of tile 1 resolved
-  Regs rk, rv;
-  int rows[Regs::NU];
-  Regs::rows(rows, src_of(0), tid);
-  rk.issue(Kg, rows, tid);
-  rv.issue(Vg, rows, tid);
-  int sflag = sep_flag(0);
-  if (n_tiles > 1) Regs::rows(rows, src_of(1), tid);
+  // prologue: the first PF tiles in flight
+  auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
+    int rows[Regs::NU];
+    Regs::rows(rows, src_of(t), tid);
+    rk.issue(Kg, rows, tid);
+    rv.issue(Vg, rows, tid);
+    sflag = sep_flag(t);
+  };
+  Regs rkA, rvA, rkB, rvB;
+  int sA = 0, sB = 0;
+  issue(0, rkA, rvA, sA);
+  if (PF == 2 && n_tiles > 1) issue(1, rkB, rvB, sB);
 
   frag qf[NQF];
 #pragma unroll
@@ -113,93 +128,115 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   const int wrow0 = q0 + 32 * w;
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
-  for (int t = 0; t < n_tiles; ++t) {
+  auto step = [&](int t, Regs& rk, Regs& rv, int& sflag) {
     const int buf = t & 1;
     rk.store(Ks[buf], tid);
     rv.store(Vs[buf], tid);
     const uint64_t sepbits = __ballot(sflag != 0);
     __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
-    if (t + 1 < n_tiles) {
-      rk.issue(Kg, rows, tid);
-      rv.issue(Vg, rows, tid);
-      sflag = sep_flag(t + 1);
-      if (t + 2 < n_tiles) Regs::rows(rows, src_of(t + 2), tid);
-    }
+    if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
     const T* K = Ks[buf];
     const T* V = Vs[buf];
 
-    // S^T = K Q^T for the two 32-key halves of the tile
+    // S^T = K Q^T for the two 32-key halves of the tile; each half's operands
+    // are read into registers first so its MFMAs issue back to back
     f32x16 sacc[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      frag kk[NQF];
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) kk[c] = read_x<T, D>(K, k2, c, lane);
       f32x16 acc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(read_x<T, D>(K, k2, c, lane), qf[c], acc);
+      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(kk[c], qf[c], acc);
       sacc[k2] = acc;
     }
 
-    // scale and mask (bit r of vis: key r of the tile is visible to this row)
-    const bool anchor_tile = t < n_at;
+    // mask (partial tiles only; bit r of vis: key r of the tile is visible)
+    const bool anchor_tile = t >= n_band;
     bool full;
     uint64_t vis;
     if (anchor_tile) {
-      const int nv = n_anchor - t * kKTile;
+      const int nv = n_anchor - (t - n_band) * kKTile;
       full = nv >= kKTile;
       vis = bit_range(0, nv - 1);
     } else {
-      const int c0 = (kb + t - n_at) * kKTile;
+      const int c0 = (kb + t) * kKTile;
       full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
       vis = band_visible(iq, c0, lo, p.S, p.a, p.n, sepbits);
     }
-    vis >>= 4 * hh;
+    if (!full) {  // wave-uniform
+      vis >>= 4 * hh;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const uint32_t vw = (uint32_t)(vis >> (32 * k2));
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint32_t vw = (uint32_t)(vis >> (32 * k2));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sv = sacc[k2][i] * p.scale_log2;
-        if (!full && !((vw >> (((i >> 2) << 3) + (i & 3))) & 1u)) sv = -INFINITY;
-        sacc[k2][i] = sv;
+        for (int i = 0; i < 16; ++i) {
+          const bool on = (vw >> (((i >> 2) << 3) + (i & 3))) & 1u;
+          sacc[k2][i] = on ? sacc[k2][i] : -INFINITY;
+        }
       }
     }
 
-    // online softmax update
-    float mloc = m;
+    // online softmax in base 2 on raw scores: p = 2^(s*c - m).  The running
+    // max m only moves when a row's max grows by more than kLazy (so p stays
+    // below 2^kLazy), which leaves the rescale of O out of most tiles.
+    float mloc = -INFINITY;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[k2][i]);
-    const float m_new = fmaxf(mloc, xor32(mloc));
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-    float psum = 0.f;
+    mloc = pair_max(mloc) * p.scale_log2;  // scale > 0
+    const bool grow = mloc > m + kLazy;
+    if (__any(grow)) {  // wave-uniform
+      // rows that grow rescale by 2^(m - mloc) (0 on their first visible tile,
+      // m = -inf); the others keep factor 1 (also when m is still -inf)
+      const float alpha = grow ? fast_exp2(m - mloc) : 1.f;
+      m = grow ? mloc : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(sacc[k2][i] - m_use);
+        const float pv = fast_exp2(__builtin_fmaf(sacc[k2][i], p.scale_log2, -m_use));
         sacc[k2][i] = pv;
-        psum += pv;
+        ps[i & 3] += pv;
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, one 32-key half at a time with its V^T operands read first
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int k2 = 0; k2 < 2; ++k2) {
+      frag vv[SPB][NDB];
+#pragma unroll
+      for (int sl = 0; sl < SPB; ++sl)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vv[sl][db] = read_xt<T, D>(V, k2, sl, 32 * db, lane);
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) {
         const frag pf = acc_frag<T>(sacc[k2], sl);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = Tr::mfma(read_xt<T, D>(V, k2, sl, 32 * db, lane), pf, oacc[db]);
+        for (int db = 0; db < NDB; ++db) oacc[db] = Tr::mfma(vv[sl][db], pf, oacc[db]);
       }
+    }
+  };
+
+  if constexpr (PF == 2) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, rkA, rvA, sA);
+      if (t + 1 < n_tiles) step(t + 1, rkB, rvB, sB);
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) step(t, rkA, rvA, sA);
   }
 
   // normalise and store
-  const float l_tot = l + xor32(l);
+  const float l_tot = pair_sum(l);
   const float inv = 1.f / l_tot;
   if (q_ok) {
     T* Og = (T*)p.o + (((size_t)b * p.Hq + h) * p.S + iq) * D;

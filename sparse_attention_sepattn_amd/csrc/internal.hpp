@@ -27,7 +27,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const AttnSha
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
 // `ev` (nullable): kBwdLaunches + 1 events recorded before the first launch
 // and after each launch, for per-kernel timing.
-constexpr int kBwdLaunches = 4;
+constexpr int kBwdLaunches = 3;
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, const AttnShape& sh, const sepattn_index& idx, void* dq,
                       void* dk, void* dv, void* ws, hipStream_t stream, hipEvent_t* ev);
