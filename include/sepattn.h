@@ -159,7 +159,8 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
  * of the three kernels: (1) row sums D = rowsum(dO * O), (2) the main kernel
  * (key-major dK/dV over gathered anchor tiles and over band tiles, and
  * query-major dQ, as one grid of independent work items), (3) the sum of the
- * anchor rows' partials.  Results are identical to sepattn_bwd. */
+ * anchor rows' partials.  A NULL entry records nothing at its point.
+ * Results are identical to sepattn_bwd. */
 int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
                          const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
@@ -215,8 +216,9 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
 
 /* sepcache_decode with per-kernel timing: `events` is a HOST array of
  * n_events >= 3 hipEvent_t (as void*), recorded on `stream` before the decode
- * kernel, after it, and after the kernel that merges its chunk partials.
- * Results are identical to sepcache_decode. */
+ * kernel, after it, and after the kernel that merges its chunk partials.  A
+ * NULL entry records nothing at its point.  Results are identical to
+ * sepcache_decode. */
 int sepcache_decode_profiled(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
                              const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                              void* stream, void* const* events, int n_events);

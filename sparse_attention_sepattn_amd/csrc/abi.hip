@@ -155,8 +155,6 @@ int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void
                          const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                          void* stream, void* const* events, int n_events) {
   if (!events || n_events < kBwdLaunches + 1) return SEPATTN_EINVAL;
-  for (int i = 0; i <= kBwdLaunches; ++i)
-    if (!events[i]) return SEPATTN_EINVAL;
   return bwd_common(q, k, v, o, lse, dout, B, Hq, Hkv, S, d, dtype, scale, idx, dq, dk, dv, ws, ws_bytes,
                     stream, (hipEvent_t*)events);
 }
@@ -207,7 +205,7 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
 int sepcache_decode_profiled(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
                              const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                              void* stream, void* const* events, int n_events) {
-  if (!events || n_events < 3 || !events[0] || !events[1] || !events[2]) return SEPATTN_EINVAL;
+  if (!events || n_events < 3) return SEPATTN_EINVAL;
   return decode_common(cache, q, Hq, rope_cos, rope_sin, scale, o, ws, ws_bytes, stream,
                        (hipEvent_t*)events);
 }

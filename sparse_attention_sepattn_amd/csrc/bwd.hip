@@ -270,9 +270,13 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
     }
     // every row of this 64-row chunk sees every key of the wave: skip the tests
     const bool full = __all(ql <= r0 && qh >= r0 + kKTile - 1);
+    // bit r: row r0 + r sees this lane's key
+    const uint64_t vis = full ? ~0ull : bit_range(ql - r0, qh - r0);
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      // 32 rows that see no key of the wave add nothing (wave-uniform skip)
+      if (!full && !__any((uint32_t)(vis >> (32 * mb)) != 0u)) continue;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
         frag qq[NF], oo[NF];  // operands first, then the MFMAs back to back
@@ -287,29 +291,27 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
           pacc = Tr::mfma(oo[c], vf[c], pacc);
         }
       }
-      // P and dS; rows are queries r0 + 32mb + acc_row(i), column is this lane's key
-      // (rows past S were loaded as zeros with zero LSE and D, so they add nothing)
+      // P, masked, then dS = P (dP - D); rows are queries r0 + 32mb + acc_row(i),
+      // the column is this lane's key (rows past S were loaded as zeros with
+      // zero LSE and D, so they add nothing)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int rl0 = 32 * mb + 8 * i4 + 4 * hh;
-        const f32x4 l4 = *(const f32x4*)&lb[rl0];
-        const f32x4 d4 = *(const f32x4*)&db_[rl0];
+        const f32x4 l4 = *(const f32x4*)&lb[32 * mb + 8 * i4 + 4 * hh];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          const float pv = fast_exp2(__builtin_fmaf(sacc[i], p.scale_log2, -l4[e]));
-          sacc[i] = pv;
-          pacc[i] = pv * (pacc[i] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) sacc[4 * i4 + e] = __builtin_fmaf(sacc[4 * i4 + e], p.scale_log2, -l4[e]);
       }
-      if (!full) {  // wave-uniform
+      if (!full) {  // wave-uniform: masked exponents become -inf, so P = 0
+        const uint32_t vw = (uint32_t)(vis >> (32 * mb + 4 * hh));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = r0 + 32 * mb + acc_row(i, hh);
-          const bool on = q >= ql && q <= qh;
-          sacc[i] = on ? sacc[i] : 0.f;
-          pacc[i] = on ? pacc[i] : 0.f;
-        }
+        for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = fast_exp2(sacc[i]);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 d4 = *(const f32x4*)&db_[32 * mb + 8 * i4 + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pacc[4 * i4 + e] = sacc[4 * i4 + e] * (pacc[4 * i4 + e] - d4[e]);
       }
       // dV^T += dO^T P ; dK^T += Q^T dS (per step: operands first, then MFMAs)
 #pragma unroll
@@ -502,12 +504,16 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
       full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
       vis = band_visible(iq, c0, lo, p.S, p.a, p.n, sepbits);
     }
-    vis >>= 4 * hh;
+    // a 32-key half that no query of the wave sees is skipped (wave-uniform)
+    bool live[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) live[k2] = full || __any((uint32_t)(vis >> (32 * k2)) != 0u);
 
     // rows past S have zero Q, dO, LSE and D, so their dS is zero unmasked
     f32x16 ds[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      if (!live[k2]) continue;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
         frag kk[NQF], vv[NQF];  // operands first, then the MFMAs back to back
@@ -523,23 +529,22 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(sacc[i], p.scale_log2, -lse2));
-        ds[k2][i] = pv * (pacc[i] - Di);
-      }
-      if (!full) {  // wave-uniform
-        const uint32_t vw = (uint32_t)(vis >> (32 * k2));
+      for (int i = 0; i < 16; ++i) sacc[i] = __builtin_fmaf(sacc[i], p.scale_log2, -lse2);
+      if (!full) {  // wave-uniform: masked exponents become -inf, so P = 0
+        const uint32_t vw = (uint32_t)(vis >> (32 * k2 + 4 * hh));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool on = (vw >> (((i >> 2) << 3) + (i & 3))) & 1u;
-          ds[k2][i] = on ? ds[k2][i] : 0.f;
-        }
+        for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = fast_exp2(sacc[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[k2][i] = sacc[i] * (pacc[i] - Di);
     }
 
-    // dQ^T += K^T dS^T, one 32-key half at a time with its K^T operands read first
+    // dQ^T += K^T dS^T, one live 32-key half at a time with its K^T operands read first
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      if (!live[k2]) continue;
       frag kt[SPB][NDB];
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl)
@@ -675,18 +680,18 @@ static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   const int main_blocks = a.n_anchor_items + a.n_dq_items + a.n_band_items;
   const int fin_rows_per_block = 256 / (D / 4);
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_blocks), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
                                                        a.B * a.Hkv),
                      dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  if (ev && ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -217,13 +217,13 @@ size_t decode_workspace_bytes(const sepcache& c, int Hq) {
 template <int D, int G>
 static hipError_t launch_decode_t(const DecArgs& a, int B, hipStream_t stream, hipEvent_t* ev) {
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3(a.nsplit, a.Hkv, B), dim3(kDecThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * a.Hq), dim3(D), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+  if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -29,8 +29,11 @@ struct FwdArgs {
 constexpr int kFwdThreads = 256;
 // Lazy rescaling threshold (base-2 units): probabilities stay below 2^8.
 constexpr float kLazy = 8.f;
+#ifndef SEPATTN_FWD_SKIP
+#define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
+#endif
 #ifndef SEPATTN_FWD_PREFETCH
-#define SEPATTN_FWD_PREFETCH 2
+#define SEPATTN_FWD_PREFETCH 1
 #endif
 
 template <typename T, int D>
@@ -138,21 +141,7 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
     const T* K = Ks[buf];
     const T* V = Vs[buf];
 
-    // S^T = K Q^T for the two 32-key halves of the tile; each half's operands
-    // are read into registers first so its MFMAs issue back to back
-    f32x16 sacc[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      frag kk[NQF];
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) kk[c] = read_x<T, D>(K, k2, c, lane);
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(kk[c], qf[c], acc);
-      sacc[k2] = acc;
-    }
-
-    // mask (partial tiles only; bit r of vis: key r of the tile is visible)
+    // visibility (partial tiles only; bit r of vis: key r of the tile is visible)
     const bool anchor_tile = t >= n_band;
     bool full;
     uint64_t vis;
@@ -165,17 +154,33 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
       full = c0 >= lo && c0 + kKTile - 1 <= wrow0 && wrow1 - c0 < p.n && c0 + kKTile - 1 < p.S;
       vis = band_visible(iq, c0, lo, p.S, p.a, p.n, sepbits);
     }
-    if (!full) {  // wave-uniform
-      vis >>= 4 * hh;
+    // a 32-key half that no query of the wave sees is skipped (wave-uniform)
+    bool live[2];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const uint32_t vw = (uint32_t)(vis >> (32 * k2));
+    for (int k2 = 0; k2 < 2; ++k2) live[k2] = full || !SEPATTN_FWD_SKIP || __any((uint32_t)(vis >> (32 * k2)) != 0u);
+
+    // S^T = K Q^T for the live 32-key halves of the tile; each half's operands
+    // are read into registers first so its MFMAs issue back to back
+    f32x16 sacc[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool on = (vw >> (((i >> 2) << 3) + (i & 3))) & 1u;
-          sacc[k2][i] = on ? sacc[k2][i] : -INFINITY;
+    for (int k2 = 0; k2 < 2; ++k2) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = -INFINITY;
+      if (live[k2]) {
+        frag kk[NQF];
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) kk[c] = read_x<T, D>(K, k2, c, lane);
+        acc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) acc = Tr::mfma(kk[c], qf[c], acc);
+        if (!full) {  // wave-uniform
+          const uint32_t vw = (uint32_t)(vis >> (32 * k2 + 4 * hh));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[i] = keep_or_neg_inf(acc[i], bit_mask(vw, acc_bit(i)));
         }
       }
+      sacc[k2] = acc;
     }
 
     // online softmax in base 2 on raw scores: p = 2^(s*c - m).  The running
@@ -200,18 +205,21 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
     const float m_use = m == -INFINITY ? 0.f : m;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int k2 = 0; k2 < 2; ++k2) {
+      if (!live[k2]) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = fast_exp2(__builtin_fmaf(sacc[k2][i], p.scale_log2, -m_use));
         sacc[k2][i] = pv;
         ps[i & 3] += pv;
       }
+    }
     l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // O^T += V^T P^T, one 32-key half at a time with its V^T operands read first
+    // O^T += V^T P^T, one live 32-key half at a time with its V^T operands read first
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      if (!live[k2]) continue;
       frag vv[SPB][NDB];
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl)

@@ -179,6 +179,19 @@ __device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
   return (~0ull >> (63 - hi)) & (~0ull << lo);
 }
 
+// Masking of one accumulator element by bit `pos` of a lane's visibility
+// word: v_bfe_i32 sign-extends the 1-bit field to an all-ones / all-zero
+// mask; a bitfield insert then keeps the value or puts -inf in its place.
+__device__ __forceinline__ uint32_t bit_mask(uint32_t w, int pos) {
+  return (uint32_t)__builtin_amdgcn_sbfe((int)w, pos, 1);
+}
+__device__ __forceinline__ float keep_or_neg_inf(float x, uint32_t m) {
+  return __uint_as_float((__float_as_uint(x) & m) | (~m & 0xFF800000u));
+}
+// Bit position, within a lane's 32-row (or 32-key) block, of accumulator
+// element i once the block's word is shifted right by 4 * (lane / 32).
+__device__ __forceinline__ constexpr int acc_bit(int i) { return ((i >> 2) << 3) + (i & 3); }
+
 // Keys c0 .. c0+63 of the band that query row iq sees (bit r = key c0 + r):
 // keys in [lo, min(iq, S-1)] that are initial (< a) or separators (sepbits),
 // plus the window [max(lo, iq - n + 1), min(iq, S-1)].

@@ -75,6 +75,14 @@ def test_argument_errors_are_host_side():
     assert need > 0
     assert L.sepattn_bwd(fake, fake, fake, fake, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st),
                          fake, fake, fake, fake, need - 1, z) == 4
+    # profiled variant: the event array is required and holds 4 entries (NULL entries are allowed)
+    ev4 = (ctypes.c_void_p * 4)()
+    assert L.sepattn_bwd_profiled(fake, fake, fake, fake, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st),
+                                  fake, fake, fake, fake, need, z, None, 4) == 1
+    assert L.sepattn_bwd_profiled(fake, fake, fake, fake, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st),
+                                  fake, fake, fake, fake, need, z, ev4, 3) == 1
+    assert L.sepattn_bwd_profiled(fake, fake, fake, fake, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st),
+                                  fake, fake, fake, fake, need - 1, z, ev4, 4) == 4
 
 
 def test_cache_capacity_errors():
