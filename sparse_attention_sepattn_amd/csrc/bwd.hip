@@ -39,9 +39,12 @@ constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
 // Workgroups per CU the register budget targets, and how many tiles ahead
 // global loads are issued: the d=128 and fp32 kernels keep more operands
 // resident than fit two waves per SIMD with two tiles in flight.
+#ifndef SEPATTN_BWD_OCC
+#define SEPATTN_BWD_OCC 2
+#endif
 template <typename T, int D>
 constexpr int bwd_occupancy() {
-  return (sizeof(T) == 2 && D == 64) ? 2 : 1;
+  return (sizeof(T) == 2 && D == 64) ? SEPATTN_BWD_OCC : 1;
 }
 #ifndef SEPATTN_DKDV_PREFETCH
 #define SEPATTN_DKDV_PREFETCH 1
@@ -74,6 +77,8 @@ struct BwdArgs {
   int B, Hq, Hkv, S, a, n, QT;
   int nchunk, chunk_tiles;  // anchor work split: nchunk chunks of chunk_tiles query tiles
   int units;                // ceil(S / 128) key units per (sequence, kv head)
+  int anchor_lanes;         // anchor work items per (sequence, kv head, chunk); each walks units
+                            // lane, lane + anchor_lanes, ... until one has no anchor a query sees
   int n_anchor_items, n_dq_items, n_band_items;
   float scale;
   float scale_log2;
@@ -139,7 +144,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
 // key-major dK/dV of one key unit (128 keys) against a range of query tiles
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool ANCHOR>
-__device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk, T* Qs, T* dOs,
+__device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk, T* Qs, T* dOs,
                                           float* lse_s, float* dd_s) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
@@ -169,7 +174,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
     const int a0 = unit * kKeysPerWG;
     const int p0 = a0 < p.S ? p.anchor_pos[(size_t)b * p.S + a0] : -1;
     const int first = p0 >= 0 ? (p0 + p.n - 1) / kQTile + 1 : p.QT;
-    if (first >= p.QT) return;  // no query sees these anchors; never read
+    if (first >= p.QT) return false;  // no query sees these anchors (nor later ones); never read
     qi_begin = max(first, chunk * p.chunk_tiles);
     qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);  // may be empty: the slot is then zero-filled
   } else {
@@ -272,48 +277,62 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
     const bool full = __all(ql <= r0 && qh >= r0 + kKTile - 1);
     // bit r: row r0 + r sees this lane's key
     const uint64_t vis = full ? ~0ull : bit_range(ql - r0, qh - r0);
+    // 32 rows that see no key of the wave add nothing (wave-uniform skip)
+    bool live[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) live[mb] = full || __any((uint32_t)(vis >> (32 * mb)) != 0u);
 
+    // S = Q K^T and dP = dO V^T for the 32-row block mb (operands first, then
+    // the MFMAs back to back)
+    auto scores = [&](int mb, f32x16& sacc, f32x16& pacc) {
+      frag qq[NF], oo[NF];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      // 32 rows that see no key of the wave add nothing (wave-uniform skip)
-      if (!full && !__any((uint32_t)(vis >> (32 * mb)) != 0u)) continue;
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      {
-        frag qq[NF], oo[NF];  // operands first, then the MFMAs back to back
-#pragma unroll
-        for (int c = 0; c < NF; ++c) {
-          qq[c] = read_x<T, D>(Qb, mb, c, lane);
-          oo[c] = read_x<T, D>(dOb, mb, c, lane);
-        }
-#pragma unroll
-        for (int c = 0; c < NF; ++c) {
-          sacc = Tr::mfma(qq[c], kf[c], sacc);
-          pacc = Tr::mfma(oo[c], vf[c], pacc);
-        }
+      for (int c = 0; c < NF; ++c) {
+        qq[c] = read_x<T, D>(Qb, mb, c, lane);
+        oo[c] = read_x<T, D>(dOb, mb, c, lane);
       }
-      // P, masked, then dS = P (dP - D); rows are queries r0 + 32mb + acc_row(i),
-      // the column is this lane's key (rows past S were loaded as zeros with
-      // zero LSE and D, so they add nothing)
+      sacc = f32x16{};
+      pacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NF; ++c) {
+        sacc = Tr::mfma(qq[c], kf[c], sacc);
+        pacc = Tr::mfma(oo[c], vf[c], pacc);
+      }
+    };
+    // P (masked exponents become -inf, so P = 0) and dS = P (dP - D), as MFMA
+    // operands; rows are queries r0 + 32mb + acc_row(i), the column is this
+    // lane's key (rows past S were loaded as zeros with zero LSE and D, so
+    // they add nothing)
+    auto probs = [&](int mb, f32x16& sacc, f32x16& pacc, frag* pf, frag* sf) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const f32x4 l4 = *(const f32x4*)&lb[32 * mb + 8 * i4 + 4 * hh];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[4 * i4 + e] = __builtin_fmaf(sacc[4 * i4 + e], p.scale_log2, -l4[e]);
       }
-      if (!full) {  // wave-uniform: masked exponents become -inf, so P = 0
+      if (!full) {  // wave-uniform
         const uint32_t vw = (uint32_t)(vis >> (32 * mb + 4 * hh));
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = fast_exp2(sacc[i]);
-#pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const f32x4 d4 = *(const f32x4*)&db_[32 * mb + 8 * i4 + 4 * hh];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pacc[4 * i4 + e] = sacc[4 * i4 + e] * (pacc[4 * i4 + e] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const float pv = fast_exp2(sacc[4 * i4 + e]);
+          sacc[4 * i4 + e] = pv;
+          pacc[4 * i4 + e] = pv * (pacc[4 * i4 + e] - d4[e]);
+        }
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS (per step: operands first, then MFMAs)
+#pragma unroll
+      for (int sl = 0; sl < SPB; ++sl) {
+        pf[sl] = acc_frag<T>(sacc, sl);
+        sf[sl] = acc_frag<T>(pacc, sl);
+      }
+    };
+    // dV^T += dO^T P ; dK^T += Q^T dS (per step: operands first, then MFMAs)
+    auto grads = [&](int mb, const frag* pf, const frag* sf) {
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) {
         frag ot[NDB], qt_[NDB];
@@ -322,14 +341,22 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
           ot[dbk] = read_xt<T, D>(dOb, mb, sl, 32 * dbk, lane);
           qt_[dbk] = read_xt<T, D>(Qb, mb, sl, 32 * dbk, lane);
         }
-        const frag pf = acc_frag<T>(sacc, sl);
-        const frag sf = acc_frag<T>(pacc, sl);
 #pragma unroll
         for (int dbk = 0; dbk < NDB; ++dbk) {
-          dv[dbk] = Tr::mfma(ot[dbk], pf, dv[dbk]);
-          dk[dbk] = Tr::mfma(qt_[dbk], sf, dk[dbk]);
+          dv[dbk] = Tr::mfma(ot[dbk], pf[sl], dv[dbk]);
+          dk[dbk] = Tr::mfma(qt_[dbk], sf[sl], dk[dbk]);
         }
       }
+    };
+
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (!live[mb]) continue;
+      f32x16 sacc, pacc;
+      frag pf[SPB], sf[SPB];
+      scores(mb, sacc, pacc);
+      probs(mb, sacc, pacc, pf, sf);
+      grads(mb, pf, sf);
     }
   };
 
@@ -343,7 +370,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
   }
 
   // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i)
-  if (krow < 0) return;
+  if (krow < 0) return true;
   float* ka = nullptr;
   float* va = nullptr;
   T* dkg = nullptr;
@@ -387,6 +414,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& p, int b, int g, int un
         *(f32x4*)(dvg + d0) = vv4;
       }
     }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -606,13 +634,16 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   int x = blockIdx.x;
   const int BG = p.B * p.Hkv;
   if (x < p.n_anchor_items) {
-    // unit-major so the few active anchor units come first
-    const int per_unit = BG * p.nchunk;
-    const int unit = x / per_unit;
-    const int r = x - unit * per_unit;
+    // lane-major so the first anchor units come first
+    const int per_lane = BG * p.nchunk;
+    const int lane0 = x / per_lane;
+    const int r = x - lane0 * per_lane;
     const int bg = r / p.nchunk;
     const int chunk = r - bg * p.nchunk;
-    dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smL, smD);
+    for (int unit = lane0; unit < p.units; unit += p.anchor_lanes) {
+      if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smL, smD)) break;
+      __syncthreads();  // the next unit refills the tile buffers
+    }
     return;
   }
   x -= p.n_anchor_items;
@@ -727,7 +758,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.a = idx.a;
   a.n = idx.n;
   a.units = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
-  a.n_anchor_items = a.units * sh.B * sh.Hkv * a.nchunk;
+  a.anchor_lanes = std::min(a.units, std::max(2, sh.S / 2048));
+  a.n_anchor_items = a.anchor_lanes * sh.B * sh.Hkv * a.nchunk;
   a.n_dq_items = sh.B * sh.Hq * a.QT;
   a.n_band_items = a.units * sh.B * sh.Hkv;
   a.scale = sh.scale;
