@@ -275,24 +275,36 @@ def decode_leg(args, torch, sa, synth):
         lens[t].copy_(cache.state)
     L = lens[:, :, :3].sum(-1).cpu().numpy().astype(np.int64)  # [T, B]
 
-    cache.init()
     ev = Events()
     stream = torch.cuda.current_stream().cuda_stream
-    marks = [ev.new(4) for _ in range(T)]
-    t0, t1 = ev.new(2)
-    torch.cuda.synchronize()
-    ev.record(t0, stream)
-    for t in range(T):
+
+    # per-kernel breakdown (events between every kernel); not the timed region
+    cache.init()
+    nb = min(T, 1024)
+    marks = [ev.new(4) for _ in range(nb)]
+    for t in range(nb):
         m = marks[t]
         ev.record(m[0], stream)
         cache.update(ks[t], vs[t], toks[t], sep)
         cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=m[1:4])
+    torch.cuda.synchronize()
+    lob = nb // 2
+    upd = np.array([ev.ms(m[0], m[1]) for m in marks])[lob:]
+    mrg = np.array([ev.ms(m[2], m[3]) for m in marks])[lob:]
+
+    # timed region: T update + decode steps; events only around the decode kernel
+    cache.init()
+    marks = [ev.new(2) for _ in range(T)]
+    t0, t1 = ev.new(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for t in range(T):
+        cache.update(ks[t], vs[t], toks[t], sep)
+        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[marks[t][0], marks[t][1], None])
     ev.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = ev.ms(t0, t1)
-    upd = np.array([ev.ms(m[0], m[1]) for m in marks])
-    dec = np.array([ev.ms(m[1], m[2]) for m in marks])
-    mrg = np.array([ev.ms(m[2], m[3]) for m in marks])
+    dec = np.array([ev.ms(m[0], m[1]) for m in marks])
     ev.close()
     lo = min(1024, T // 4)
     kv_bytes = (L * Hkv * d * 2 * 2).sum(axis=1)          # K and V rows, every slot, every kv head
@@ -301,17 +313,18 @@ def decode_leg(args, torch, sa, synth):
     dec_bytes = kv_bytes + q_bytes + table_bytes            # per decode-kernel launch
     gbs = dec_bytes[lo:].sum() / (dec[lo:].sum() * 1e-3) / 1e9
     step_bytes = kv_bytes + 2 * q_bytes + B * Hkv * d * 2 * 2 + B * 4
-    step_ms = (upd + dec + mrg)[lo:]
+    step_ms = total_ms / T
     traffic = traffic_from_profiles("decode_kernel")
     return dict(
         workload="SepCache streaming decode: B64, 32 q / 8 kv heads, d128, bf16, c=800 (a4 s64 w256), "
                  "RoPE theta 500000 by slot, p_sep 0.08",
         steps=T, steady_from=lo, mean_cached_slots=round(float(L[lo:].mean()), 1),
-        decode_kernel_us=round(float(dec[lo:].mean()) * 1e3, 3), merge_kernel_us=round(float(mrg[lo:].mean()) * 1e3, 3),
-        update_kernel_us=round(float(upd[lo:].mean()) * 1e3, 3),
-        us_per_step=round(float(step_ms.mean()) * 1e3, 3), loop_ms_total=round(total_ms, 3),
+        decode_kernel_us=round(float(dec[lo:].mean()) * 1e3, 3),
+        merge_kernel_us_untimed_pass=round(float(mrg.mean()) * 1e3, 3),
+        update_kernel_us_untimed_pass=round(float(upd.mean()) * 1e3, 3),
+        us_per_step=round(step_ms * 1e3, 3), loop_ms_total=round(total_ms, 3),
         value=round(float(gbs), 1), unit="GB/s",
-        step_GBps=round(float(step_bytes[lo:].sum() / (step_ms.sum() * 1e-3) / 1e9), 1),
+        step_GBps=round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
         roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(float(gbs), 1), peak=PEAK_HBM_GBS,
                       unit="GB/s", frac=round(float(gbs) / PEAK_HBM_GBS, 4), traffic=traffic,
                       algorithmic_MB_per_launch=round(float(dec_bytes[lo:].mean()) / 1e6, 3)),

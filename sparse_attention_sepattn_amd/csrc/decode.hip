@@ -16,7 +16,10 @@
 namespace sepattn {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecChunk = 128;
+#ifndef SEPATTN_DEC_CHUNK
+#define SEPATTN_DEC_CHUNK 128
+#endif
+constexpr int kDecChunk = SEPATTN_DEC_CHUNK;
 
 struct DecArgs {
   const uint16_t* k;
@@ -185,7 +188,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecArgs p) {
   }
 }
 
-// Merge the chunk partials of every (sequence, query head).
+// Merge the chunk partials of every (sequence, query head): one pass with a
+// running maximum, the partials of 8 chunks loaded together.
 template <int D>
 __global__ void __launch_bounds__(D) decode_combine_kernel(DecArgs p) {
   const int bh = blockIdx.x;
@@ -195,14 +199,31 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(DecArgs p) {
   const int L = st[0] + st[1] + st[2];
   const int used = (L + kDecChunk - 1) / kDecChunk;
   const float* part = p.ws + (size_t)bh * p.nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < used; ++s) M = fmaxf(M, part[(size_t)s * (D + 2) + D]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < used; ++s) {
-    const float* ps = part + (size_t)s * (D + 2);
-    const float wgt = fast_exp2(ps[D] - M);
-    num += wgt * ps[dd];
-    den += wgt * ps[D + 1];
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < used; s0 += 8) {
+    float m8[8], l8[8], o8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = s0 + k < used;
+      const float* ps = part + (size_t)(s0 + k) * (D + 2);
+      m8[k] = ok ? ps[D] : -INFINITY;
+      l8[k] = ok ? ps[D + 1] : 0.f;
+      o8[k] = ok ? ps[dd] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, m8[k]);
+    // chunks that were empty or fully underflowed carry -inf / 0 and add nothing
+    const float r = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    num *= r;
+    den *= r;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = m8[k] == -INFINITY ? 0.f : fast_exp2(m8[k] - Mn);
+      num += w * o8[k];
+      den += w * l8[k];
+    }
+    M = Mn;
   }
   p.o[(size_t)bh * D + dd] = f32_to_bf16_bits(num / den);
 }
