@@ -106,8 +106,9 @@ def schedule_counts(qtile, sep_prefix, a, n, S, tk=64):
 
 
 def traffic_from_profiles(kernel):
-    """HBM bytes per launch from the committed counter summary of `kernel`,
-    if it was taken on the current kernel source; else None."""
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a known-size copy), if it was taken
+    on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -117,10 +118,11 @@ def traffic_from_profiles(kernel):
             rec = json.load(f).get(kernel)
         if not rec:
             return None
-        src = os.path.join(ROOT, "sparse_attention_sepattn_amd", "csrc", rec["source"])
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-        if digest != rec["source_sha256"]:
+        h = hashlib.sha256()
+        for src in rec["source"]:
+            with open(os.path.join(ROOT, "sparse_attention_sepattn_amd", "csrc", src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"]:
             return None
         return rec["bytes_per_launch"]
     except Exception:
@@ -280,7 +282,7 @@ def decode_leg(args, torch, sa, synth):
 
     # per-kernel breakdown (events between every kernel); not the timed region
     cache.init()
-    nb = min(T, 1024)
+    nb = min(T, args.decode_breakdown_steps)
     marks = [ev.new(4) for _ in range(nb)]
     for t in range(nb):
         m = marks[t]
@@ -289,8 +291,8 @@ def decode_leg(args, torch, sa, synth):
         cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=m[1:4])
     torch.cuda.synchronize()
     lob = nb // 2
-    upd = np.array([ev.ms(m[0], m[1]) for m in marks])[lob:]
-    mrg = np.array([ev.ms(m[2], m[3]) for m in marks])[lob:]
+    upd = np.array([ev.ms(m[0], m[1]) for m in marks][lob:])
+    mrg = np.array([ev.ms(m[2], m[3]) for m in marks][lob:])
 
     # timed region: T update + decode steps; events only around the decode kernel
     cache.init()
@@ -320,8 +322,8 @@ def decode_leg(args, torch, sa, synth):
                  "RoPE theta 500000 by slot, p_sep 0.08",
         steps=T, steady_from=lo, mean_cached_slots=round(float(L[lo:].mean()), 1),
         decode_kernel_us=round(float(dec[lo:].mean()) * 1e3, 3),
-        merge_kernel_us_untimed_pass=round(float(mrg.mean()) * 1e3, 3),
-        update_kernel_us_untimed_pass=round(float(upd.mean()) * 1e3, 3),
+        merge_kernel_us_untimed_pass=round(float(mrg.mean()) * 1e3, 3) if nb else None,
+        update_kernel_us_untimed_pass=round(float(upd.mean()) * 1e3, 3) if nb else None,
         us_per_step=round(step_ms * 1e3, 3), loop_ms_total=round(total_ms, 3),
         value=round(float(gbs), 1), unit="GB/s",
         step_GBps=round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
@@ -368,6 +370,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--decode-breakdown-steps", type=int, default=1024,
+                    help="steps of the untimed per-kernel breakdown pass of the decode leg (0: none)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
