@@ -14,6 +14,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int to_status(hipError_t e) { return e == hipSuccess ? SEPATTN_OK : SEPATTN_EHIP; }
 
+// Launch failures are read with hipGetLastError after each launch; an error
+// an unrelated earlier HIP call left behind on this thread is cleared first
+// so it is not reported as ours.
+void forget_stale_error() { (void)hipGetLastError(); }
+
 int make_sepset(const int32_t* sep_ids, int n_sep, SepSet* out) {
   if (n_sep < 0 || n_sep > SEPATTN_MAX_SEP_IDS) return SEPATTN_EINVAL;
   if (n_sep > 0 && !sep_ids) return SEPATTN_EINVAL;
@@ -111,6 +116,7 @@ int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* s
   if (st != SEPATTN_OK) return st;
   idx->a = a;
   idx->n = n;
+  forget_stale_error();
   return to_status(launch_build_index(token_ids, B, S, sep, a, n, *idx, (hipStream_t)stream));
 }
 
@@ -120,6 +126,7 @@ int sepattn_fwd(const void* q, const void* k, const void* v, int B, int Hq, int 
   if (st != SEPATTN_OK) return st;
   if (!q || !k || !v || !o || !lse || !index_ok(idx, B, S)) return SEPATTN_EINVAL;
   AttnShape sh{B, Hq, Hkv, S, d, dtype, scale};
+  forget_stale_error();
   return to_status(launch_fwd(q, k, v, sh, *idx, o, lse, (hipStream_t)stream));
 }
 
@@ -139,6 +146,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
   if (!ws || ((uintptr_t)ws & 255) != 0) return SEPATTN_EINVAL;
   if (ws_bytes < bwd_workspace_bytes(B, Hq, Hkv, S, d)) return SEPATTN_EWORKSPACE;
   AttnShape sh{B, Hq, Hkv, S, d, dtype, scale};
+  forget_stale_error();
   return to_status(launch_bwd(q, k, v, o, lse, dout, sh, *idx, dq, dk, dv, ws, (hipStream_t)stream, ev));
 }
 
@@ -162,6 +170,7 @@ int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void
 int sepcache_init(const sepcache* cache, void* stream) {
   int st = check_cache(cache);
   if (st != SEPATTN_OK) return st;
+  forget_stale_error();
   return to_status(launch_cache_init(*cache, (hipStream_t)stream));
 }
 
@@ -173,6 +182,7 @@ int sepcache_update(const sepcache* cache, const void* k_new, const void* v_new,
   SepSet sep;
   st = make_sepset(sep_ids, n_sep, &sep);
   if (st != SEPATTN_OK) return st;
+  forget_stale_error();
   return to_status(launch_cache_update(*cache, k_new, v_new, tok_new, sep, (hipStream_t)stream));
 }
 
@@ -192,6 +202,7 @@ static int decode_common(const sepcache* cache, const void* q, int Hq, const flo
   if (G > kMaxDecodeGroup || (G & (G - 1)) != 0) return SEPATTN_EUNSUPPORTED;
   if (!ws || ((uintptr_t)ws & 255) != 0) return SEPATTN_EINVAL;
   if (ws_bytes < decode_workspace_bytes(*cache, Hq)) return SEPATTN_EWORKSPACE;
+  forget_stale_error();
   return to_status(
       launch_decode(*cache, q, Hq, rope_cos, rope_sin, scale, o, ws, (hipStream_t)stream, ev));
 }

@@ -49,6 +49,12 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_DKDV_PREFETCH
 #define SEPATTN_DKDV_PREFETCH 1
 #endif
+#ifndef SEPATTN_DQ_DMA
+#define SEPATTN_DQ_DMA 1  // dQ: K/V tiles loaded straight into LDS
+#endif
+#ifndef SEPATTN_DQ_INTERLEAVE
+#define SEPATTN_DQ_INTERLEAVE 1  // interleaved order when both 32-key halves of a tile are live
+#endif
 #ifndef SEPATTN_DQ_PREFETCH
 #define SEPATTN_DQ_PREFETCH 1
 #endif
@@ -431,7 +437,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   constexpr int NQF = D / KSTEP;
   constexpr int NDB = D / 32;
   constexpr int SPB = 32 / KSTEP;
-  constexpr int PF = bwd_prefetch<T, D, false>();
+  constexpr bool kDMA = SEPATTN_DQ_DMA;  // K/V tiles go global -> LDS directly
+  constexpr int PF = kDMA ? 1 : bwd_prefetch<T, D, false>();
+  typedef TileDMA<T, D, kBwdThreads> DMA;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -472,11 +480,18 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     }
     return r;
   };
+  const unsigned kv_bytes = (unsigned)((size_t)p.S * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t Krs = buffer_rsrc(Kg, kv_bytes), Vrs = buffer_rsrc(Vg, kv_bytes);
   auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
     int rows[Regs::NU];
     Regs::rows(rows, src_of(t), tid);
-    rk.issue(Kg, rows, tid);
-    rv.issue(Vg, rows, tid);
+    if constexpr (kDMA) {
+      DMA::issue(Krs, kv_bytes, rows, Ks + (t & 1) * G::ELEMS, tid);
+      DMA::issue(Vrs, kv_bytes, rows, Vs + (t & 1) * G::ELEMS, tid);
+    } else {
+      rk.issue(Kg, rows, tid);
+      rv.issue(Vg, rows, tid);
+    }
     sflag = 0;
     if (t < n_band) {
       const int j = (kb + t) * kKTile + lane;
@@ -514,9 +529,12 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     const int buf = t & 1;
     T* K = Ks + buf * G::ELEMS;
     T* V = Vs + buf * G::ELEMS;
-    rk.store(K, tid);
-    rv.store(V, tid);
+    if constexpr (!kDMA) {
+      rk.store(K, tid);
+      rv.store(V, tid);
+    }
     const uint64_t sepbits = __ballot(sflag != 0);
+    if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
     __syncthreads();
     if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
 
@@ -537,52 +555,71 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) live[k2] = full || __any((uint32_t)(vis >> (32 * k2)) != 0u);
 
-    // rows past S have zero Q, dO, LSE and D, so their dS is zero unmasked
-    f32x16 ds[2];
+    // rows past S have zero Q, dO, LSE and D, so their dS is zero unmasked.
+    // S^T = K Q^T and dP^T = V dO^T for the 32-key half k2 (operands first,
+    // then the MFMAs back to back)
+    auto scores = [&](int k2, f32x16& sacc, f32x16& pacc) {
+      frag kk[NQF], vv[NQF];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      if (!live[k2]) continue;
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      {
-        frag kk[NQF], vv[NQF];  // operands first, then the MFMAs back to back
-#pragma unroll
-        for (int c = 0; c < NQF; ++c) {
-          kk[c] = read_x<T, D>(K, k2, c, lane);
-          vv[c] = read_x<T, D>(V, k2, c, lane);
-        }
-#pragma unroll
-        for (int c = 0; c < NQF; ++c) {
-          sacc = Tr::mfma(kk[c], qf[c], sacc);
-          pacc = Tr::mfma(vv[c], of[c], pacc);
-        }
+      for (int c = 0; c < NQF; ++c) {
+        kk[c] = read_x<T, D>(K, k2, c, lane);
+        vv[c] = read_x<T, D>(V, k2, c, lane);
       }
+      sacc = f32x16{};
+      pacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        sacc = Tr::mfma(kk[c], qf[c], sacc);
+        pacc = Tr::mfma(vv[c], of[c], pacc);
+      }
+    };
+    // dS^T = P^T (dP^T - D) as MFMA operands (masked exponents become -inf, so P = 0)
+    auto dsfrags = [&](int k2, f32x16& sacc, f32x16& pacc, frag* sf) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_fmaf(sacc[i], p.scale_log2, -lse2);
-      if (!full) {  // wave-uniform: masked exponents become -inf, so P = 0
+      if (!full) {  // wave-uniform
         const uint32_t vw = (uint32_t)(vis >> (32 * k2 + 4 * hh));
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = fast_exp2(sacc[i]);
+      for (int i = 0; i < 16; ++i) pacc[i] = fast_exp2(sacc[i]) * (pacc[i] - Di);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[k2][i] = sacc[i] * (pacc[i] - Di);
-    }
-
-    // dQ^T += K^T dS^T, one live 32-key half at a time with its K^T operands read first
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      if (!live[k2]) continue;
+      for (int sl = 0; sl < SPB; ++sl) sf[sl] = acc_frag<T>(pacc, sl);
+    };
+    // dQ^T += K^T dS^T with the K^T operands of the half read first
+    auto dqmm = [&](int k2, const frag* sf) {
       frag kt[SPB][NDB];
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) kt[sl][db] = read_xt<T, D>(K, k2, sl, 32 * db, lane);
 #pragma unroll
-      for (int sl = 0; sl < SPB; ++sl) {
-        const frag sf = acc_frag<T>(ds[k2], sl);
+      for (int sl = 0; sl < SPB; ++sl)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[sl][db], sf, dq[db]);
+        for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[sl][db], sf[sl], dq[db]);
+    };
+
+    if (SEPATTN_DQ_INTERLEAVE && live[0] && live[1]) {
+      // half 1's scores enter the MFMA pipe before half 0's dQ products, and
+      // half 1's exponentials overlap those products
+      f32x16 s0, p0, s1, p1;
+      frag sf0[SPB], sf1[SPB];
+      scores(0, s0, p0);
+      dsfrags(0, s0, p0, sf0);
+      scores(1, s1, p1);
+      dqmm(0, sf0);
+      dsfrags(1, s1, p1, sf1);
+      dqmm(1, sf1);
+    } else {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if (!live[k2]) continue;
+        f32x16 sacc, pacc;
+        frag sf[SPB];
+        scores(k2, sacc, pacc);
+        dsfrags(k2, sacc, pacc, sf);
+        dqmm(k2, sf);
       }
     }
   };

@@ -32,12 +32,18 @@ constexpr float kLazy = 8.f;
 #ifndef SEPATTN_FWD_SKIP
 #define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
 #endif
+#ifndef SEPATTN_FWD_OCC
+#define SEPATTN_FWD_OCC 4  // workgroups per CU the bf16 register budget targets
+#endif
+#ifndef SEPATTN_FWD_DMA
+#define SEPATTN_FWD_DMA 1  // K/V tiles loaded straight into LDS
+#endif
 #ifndef SEPATTN_FWD_PREFETCH
 #define SEPATTN_FWD_PREFETCH 1
 #endif
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kernel(FwdArgs p) {
+__global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? SEPATTN_FWD_OCC : 1) fwd_kernel(FwdArgs p) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kFwdThreads> Regs;
@@ -47,7 +53,9 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   constexpr int NQF = D / KSTEP;   // Q fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of O^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps per 32-key block
-  constexpr int PF = (sizeof(T) == 2 && D == 64) ? SEPATTN_FWD_PREFETCH : 1;  // tiles in flight
+  constexpr bool kDMA = SEPATTN_FWD_DMA;  // tiles go global -> LDS directly
+  constexpr int PF = kDMA ? 1 : ((sizeof(T) == 2 && D == 64) ? SEPATTN_FWD_PREFETCH : 1);  // tiles in flight
+  typedef TileDMA<T, D, kFwdThreads> DMA;
 
   __shared__ __attribute__((aligned(16))) T Ks[2][G::ELEMS];
   __shared__ __attribute__((aligned(16))) T Vs[2][G::ELEMS];
@@ -80,6 +88,8 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   const T* Qg = (const T*)p.q + (((size_t)b * p.Hq + h) * p.S) * D;
   const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
   const T* Vg = (const T*)p.v + (((size_t)b * p.Hkv + g) * p.S) * D;
+  const unsigned kv_bytes = (unsigned)((size_t)p.S * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t Krs = buffer_rsrc(Kg, kv_bytes), Vrs = buffer_rsrc(Vg, kv_bytes);
   const int32_t* anc = p.anchor_pos + (size_t)b * p.S;
   const uint8_t* sepf = p.is_sep + (size_t)b * p.S;
 
@@ -106,8 +116,13 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
   auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
     int rows[Regs::NU];
     Regs::rows(rows, src_of(t), tid);
-    rk.issue(Kg, rows, tid);
-    rv.issue(Vg, rows, tid);
+    if constexpr (kDMA) {
+      DMA::issue(Krs, kv_bytes, rows, Ks[t & 1], tid);
+      DMA::issue(Vrs, kv_bytes, rows, Vs[t & 1], tid);
+    } else {
+      rk.issue(Kg, rows, tid);
+      rv.issue(Vg, rows, tid);
+    }
     sflag = sep_flag(t);
   };
   Regs rkA, rvA, rkB, rvB;
@@ -133,9 +148,12 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1) fwd_kerne
 
   auto step = [&](int t, Regs& rk, Regs& rv, int& sflag) {
     const int buf = t & 1;
-    rk.store(Ks[buf], tid);
-    rv.store(Vs[buf], tid);
+    if constexpr (!kDMA) {
+      rk.store(Ks[buf], tid);
+      rv.store(Vs[buf], tid);
+    }
     const uint64_t sepbits = __ballot(sflag != 0);
+    if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
     __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
     if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
     const T* K = Ks[buf];

@@ -131,6 +131,44 @@ struct TileRegs {
   }
 };
 
+// The same 64-row tile loaded straight from global memory into LDS
+// (buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at
+// M0 + 16*l), so no registers hold the tile in flight.  A wave's instruction
+// u fills 1 KB of LDS, the rows TileRegs::row_of gives its lanes; each lane
+// fetches the global chunk that the swizzle puts at its LDS position.  Rows
+// with srow < 0 use an offset past the buffer's size, which the hardware
+// range check turns into zeros.  Completion is counted by vmcnt: the caller
+// waits (s_waitcnt vmcnt) before the barrier that publishes the tile.
+template <typename T, int D, int NT>
+struct TileDMA {
+  typedef TileGeom<T, D> G;
+  typedef TileRegs<T, D, NT> R;
+  static constexpr int NU = R::NU;
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned src_bytes, const int* srow,
+                                               T* tile, int tid) {
+    const int w = tid / kWave, lane = tid % kWave;
+    const int pos = tid % G::CH;  // 16-byte position of this lane in its LDS row
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int r = R::row_of(tid, u);
+      const int f = G::CH >= 16 ? swz16(r) : swz8(r);
+      const int c = (pos ^ f) & (G::CH - 1);
+      const unsigned off = srow[u] >= 0 ? (unsigned)(srow[u] * D + c * Traits<T>::VEC) * (unsigned)sizeof(T)
+                                        : src_bytes;
+      T* dst = tile + (w * 1024 + u * NT * 16) / (int)sizeof(T);
+      (void)lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+    }
+  }
+};
+
+// Buffer resource over `bytes` bytes from `base` (raw, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+// Waits for this wave's outstanding vector-memory loads, LDS-bound ones included.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
