@@ -40,6 +40,21 @@ def separator_flags(tok, sep_ids):
     return out
 
 
+def interval_flags(S, m):
+    """Anchor flags of the fixed-interval baseline (FixLLM): the pages compare
+    SepLLM with a variant that keeps tokens at fixed intervals instead of
+    separators (beiduofen.top, "Performance in the Spotlight: Experimental
+    Results"; atlas.scime.ai, "Measured effects reported in the paper" and
+    "Surprising findings").  Neither page gives the interval or its phase;
+    the reading taken: position ``j`` is an anchor iff ``j % m == m - 1`` (the
+    last token of every ``m``-token segment, as a separator ends its
+    segment), for an interval ``m >= 1`` the caller chooses."""
+    if m < 1:
+        raise ValueError("interval m must be >= 1")
+    j = np.arange(S, dtype=np.int64)
+    return (j % m) == (m - 1)
+
+
 def mask_rows(sep, a, n, rows):
     """Rows ``rows`` of the SepLLM mask for one sequence whose separator flags
     are ``sep`` (bool [S]).
@@ -97,9 +112,15 @@ def build_index(tok, sep_ids, a, n, tq=128, tk=64):
       1 otherwise.
     """
     tok = np.asarray(tok).reshape(-1)
-    S = tok.shape[0]
-    sep = separator_flags(tok, sep_ids)
+    return build_index_from_flags(separator_flags(tok, sep_ids), a, n, tq, tk)
 
+
+def build_index_from_flags(sep, a, n, tq=128, tk=64):
+    """``build_index`` for given anchor flags ``sep`` (bool [S]): the
+    separator flags of a token sequence, or the fixed-interval flags of
+    ``interval_flags``."""
+    sep = np.asarray(sep, dtype=bool).reshape(-1)
+    S = sep.shape[0]
     sep_prefix = np.zeros(S + 1, dtype=np.int64)
     running = 0
     for x in range(S + 1):

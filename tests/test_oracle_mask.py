@@ -149,3 +149,47 @@ def test_kept_entries_counts_tiles():
     nnz = sepmask.row_nnz(np.isin(tok, [0, 5]), 4, 64).sum()
     assert nnz <= E  # kept tiles cover every visible entry
     assert E == sum(int(r[5]) * 64 * int(r[4]) for r in idx["qtile"])
+
+
+# ---- fixed-interval anchors (the FixLLM baseline) ---------------------------
+
+@pytest.mark.parametrize("S,m,a", [(1, 1, 0), (37, 1, 2), (300, 12, 4), (300, 7, 9), (129, 200, 3), (512, 64, 0)])
+def test_interval_prefix_closed_form(S, m, a):
+    """#{j in [a, x) : j % m == m - 1} = floor(x/m) - floor(a/m) for x >= a."""
+    ix = sepmask.build_index_from_flags(sepmask.interval_flags(S, m), a, 64)
+    x = np.arange(S + 1)
+    expect = np.where(x >= a, x // m - a // m, 0)
+    assert np.array_equal(ix["sep_prefix"], expect)
+    assert ix["anchor_count"] == min(a, S) + max(0, S // m - a // m) * (S > a)
+
+
+def test_interval_every_token_is_dense_causal():
+    """m = 1 makes every token an anchor: the mask is the causal mask."""
+    S = 97
+    sep = sepmask.interval_flags(S, 1)
+    M = sepmask.mask_rows(sep, 2, 5, np.arange(S))
+    assert np.array_equal(M, np.tril(np.ones((S, S), dtype=bool)))
+
+
+def test_interval_beyond_length_is_sink_plus_window():
+    """m > S leaves no interval anchor: initial tokens plus the window only."""
+    S, a, n = 150, 3, 20
+    sep = sepmask.interval_flags(S, S + 1)
+    nnz = sepmask.mask_rows(sep, a, n, np.arange(S)).sum(axis=1)
+    i = np.arange(S)
+    lo = np.maximum(0, i - n + 1)
+    assert np.array_equal(nnz, np.minimum(a, lo) + (i - lo + 1))
+
+
+@pytest.mark.parametrize("S,m", [(200, 5), (333, 12)])
+def test_interval_index_equals_token_index(S, m):
+    """The flag path agrees with the token path on a sequence whose separator
+    ids sit exactly at the interval positions."""
+    sep_id = 7
+    tok = np.where(np.arange(S) % m == m - 1, sep_id, 100)
+    a, n = 4, 32
+    x = sepmask.build_index_from_flags(sepmask.interval_flags(S, m), a, n)
+    y = sepmask.build_index(tok, [sep_id], a, n)
+    for key in ("is_sep", "sep_prefix", "anchor_pos", "qtile", "tile_class"):
+        assert np.array_equal(x[key], y[key]), key
+    assert x["anchor_count"] == y["anchor_count"]
