@@ -128,6 +128,15 @@ int sepattn_index_bind(void* buf, size_t bytes, int B, int S, sepattn_index* idx
 int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* sep_ids, int n_sep,
                         int a, int n, sepattn_index* idx, void* stream);
 
+/* Index of the fixed-interval baseline (FixLLM: anchors at fixed intervals
+ * instead of separators; beiduofen.top, "Performance in the Spotlight:
+ * Experimental Results"; atlas.scime.ai, "Surprising findings").  Position j
+ * is an anchor iff j % interval == interval - 1 (interval >= 1), besides the
+ * `a` initial tokens; no token ids are read.  Same outputs, binding rules and
+ * errors as sepattn_build_index (EINVAL for interval < 1); sepattn_fwd and
+ * sepattn_bwd take the result unchanged. */
+int sepattn_build_index_interval(int B, int S, int interval, int a, int n, sepattn_index* idx, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Attention over the full sequence (training / prefill)                     */
 /* ------------------------------------------------------------------------ */

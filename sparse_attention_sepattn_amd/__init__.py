@@ -55,6 +55,7 @@ class _Cache(ctypes.Structure):
 
 
 EXPORTS = ["sepattn_strerror", "sepattn_index_bytes", "sepattn_index_bind", "sepattn_build_index",
+           "sepattn_build_index_interval",
            "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepattn_bwd_profiled",
            "sepcache_init", "sepcache_update",
            "sepcache_decode_workspace", "sepcache_decode", "sepcache_decode_profiled",
@@ -80,6 +81,8 @@ def load_library(path=None):
     L.sepattn_index_bind.argtypes = [vp, sz, i32, i32, ctypes.POINTER(_Index)]
     L.sepattn_build_index.restype = i32
     L.sepattn_build_index.argtypes = [vp, i32, i32, vp, i32, i32, i32, ctypes.POINTER(_Index), vp]
+    L.sepattn_build_index_interval.restype = i32
+    L.sepattn_build_index_interval.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Index), vp]
     L.sepattn_fwd.restype = i32
     L.sepattn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(_Index),
                               vp, vp, vp]
@@ -190,6 +193,16 @@ def build_index(tok, sep_ids, a, n, index=None):
     ids, ids_p = _host_ids(sep_ids)
     _check(load_library().sepattn_build_index(_ptr(tok), B, S, ids_p, len(ids), a, n,
                                               ctypes.byref(index.st), _stream()), "build_index")
+    return index
+
+
+def build_index_interval(B, S, interval, a, n, index=None, device=None):
+    """Index with anchors at fixed intervals (position j is an anchor iff
+    j % interval == interval - 1) besides the ``a`` initial tokens."""
+    if index is None:
+        index = Index(B, S, device=device if device is not None else torch.device("cuda", torch.cuda.current_device()))
+    _check(load_library().sepattn_build_index_interval(B, S, int(interval), a, n, ctypes.byref(index.st), _stream()),
+           "build_index_interval")
     return index
 
 

@@ -117,7 +117,20 @@ int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* s
   idx->a = a;
   idx->n = n;
   forget_stale_error();
-  return to_status(launch_build_index(token_ids, B, S, sep, a, n, *idx, (hipStream_t)stream));
+  return to_status(launch_build_index(token_ids, B, S, sep, 0, a, n, *idx, (hipStream_t)stream));
+}
+
+int sepattn_build_index_interval(int B, int S, int interval, int a, int n, sepattn_index* idx, void* stream) {
+  if (!idx || B < 1 || S < 1 || interval < 1 || a < 0 || n < 1) return SEPATTN_EINVAL;
+  if (idx->B != B || idx->S != S || !idx->is_sep || !idx->sep_prefix || !idx->anchor_pos ||
+      !idx->anchor_count || !idx->qtile || !idx->tile_class)
+    return SEPATTN_EINVAL;
+  SepSet none;
+  memset(&none, 0, sizeof(none));
+  idx->a = a;
+  idx->n = n;
+  forget_stale_error();
+  return to_status(launch_build_index(nullptr, B, S, none, interval, a, n, *idx, (hipStream_t)stream));
 }
 
 int sepattn_fwd(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int S, int d,

@@ -4,6 +4,11 @@
 //
 // The mask (SepLLM summary on atlas.scime.ai, "Approach"): query i sees key j
 // iff j <= i and (j < a or tok[j] is a separator or i - j < n).
+//
+// Fixed-interval anchors (the FixLLM baseline the pages compare against:
+// beiduofen.top, "Performance in the Spotlight"; atlas.scime.ai, "Surprising
+// findings"): with interval m > 0 the membership test is j % m == m - 1 and
+// no token ids are read; everything downstream is unchanged.
 #include "internal.hpp"
 
 namespace sepattn {
@@ -14,7 +19,7 @@ constexpr int kScanItems = 8;  // consecutive tokens per thread per chunk
 // One workgroup per sequence.  Chunks of kScanThreads * kScanItems tokens are
 // scanned in order with a running carry, so the result is deterministic.
 __global__ void __launch_bounds__(kScanThreads)
-index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep,
+index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep, int interval,
                   uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_prefix,
                   int32_t* __restrict__ anchor_pos, int32_t* __restrict__ anchor_count) {
   const int b = blockIdx.x;
@@ -25,7 +30,7 @@ index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep,
   __shared__ int wave_sum[kWaves];
   __shared__ int carry_sh;
 
-  const int32_t* tk = tok + (size_t)b * S;
+  const int32_t* tk = tok ? tok + (size_t)b * S : nullptr;
   uint8_t* fl = is_sep + (size_t)b * S;
   int32_t* pre = sep_prefix + (size_t)b * (S + 1);
   int32_t* anc = anchor_pos + (size_t)b * S;
@@ -43,7 +48,7 @@ index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep,
       const int j = j0 + e;
       int s = 0;
       if (j < S) {
-        s = is_separator(sep, tk[j]) ? 1 : 0;
+        s = interval > 0 ? (j % interval == interval - 1) : (is_separator(sep, tk[j]) ? 1 : 0);
         fl[j] = (uint8_t)s;
       }
       f[e] = (j < S && j >= a) ? s : 0;  // separators counted from position a on
@@ -155,9 +160,9 @@ index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
   }
 }
 
-hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int a, int n,
+hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int interval, int a, int n,
                               const sepattn_index& idx, hipStream_t stream) {
-  hipLaunchKernelGGL(index_scan_kernel, dim3(B), dim3(kScanThreads), 0, stream, tok, S, a, sep,
+  hipLaunchKernelGGL(index_scan_kernel, dim3(B), dim3(kScanThreads), 0, stream, tok, S, a, sep, interval,
                      idx.is_sep, idx.sep_prefix, idx.anchor_pos, idx.anchor_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -13,7 +13,7 @@ constexpr int kMaxCacheHeads = 128;
 // Largest number of query heads per kv head in decode.
 constexpr int kMaxDecodeGroup = 8;
 
-hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int a, int n,
+hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int interval, int a, int n,
                               const sepattn_index& idx, hipStream_t stream);
 
 struct AttnShape {

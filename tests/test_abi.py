@@ -70,6 +70,9 @@ def test_argument_errors_are_host_side():
     assert L.sepattn_build_index(fake, 1, 64, ids, 3, 4, 0, ctypes.byref(st), z) == 1
     assert L.sepattn_build_index(fake, 1, 64, ids, 3, -1, 4, ctypes.byref(st), z) == 1
     assert L.sepattn_build_index(fake, 1, 64, ids, 65, 4, 4, ctypes.byref(st), z) == 1
+    # fixed-interval index: interval < 1, index bound for another shape
+    assert L.sepattn_build_index_interval(1, 64, 0, 4, 4, ctypes.byref(st), z) == 1
+    assert L.sepattn_build_index_interval(1, 128, 12, 4, 4, ctypes.byref(st), z) == 1
     # bwd workspace too small
     need = L.sepattn_bwd_workspace(1, 2, 1, 64, 64, 1)
     assert need > 0
