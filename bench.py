@@ -333,6 +333,8 @@ def decode_leg(args, torch, sa, synth):
     fdec = np.array([ev.ms(fmarks[t][0], fmarks[t][1]) for t in sampled])
     del scratch, flush_sink
     ev.close()
+    handoff = prefill_handoff(torch, sa, synth, cfg, sep, cos.device)
+
     kv_bytes = (L * Hkv * d * 2 * 2).sum(axis=1)          # K and V rows, every slot, every kv head
     q_bytes = B * Hq * d * 2
     table_bytes = c * (d // 2) * 4 * 2
@@ -354,11 +356,44 @@ def decode_leg(args, torch, sa, synth):
         update_kernel_us_untimed_pass=round(float(upd.mean()) * 1e3, 3) if nb else None,
         us_per_step=round(step_ms * 1e3, 3), loop_ms_total=round(total_ms, 3),
         value=round(float(gbs), 1), unit="GB/s",
+        prefill_handoff=handoff,
         step_GBps=round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
         roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(float(gbs), 1), peak=PEAK_HBM_GBS,
                       unit="GB/s", frac=round(float(gbs) / PEAK_HBM_GBS, 4), traffic=traffic,
                       algorithmic_MB_per_launch=round(float(dec_bytes[sampled].mean()) / 1e6, 3)),
     )
+
+
+def prefill_handoff(torch, sa, synth, cfg, sep, dev, P=4096, reps=20):
+    """sepcache_prefill of a P-token prompt per sequence (its index built
+    beforehand, as the prefill pass has it): time per call and the bytes it
+    moves (each kept K/V row read once and written once, plus pos/tok)."""
+    B, Hkv, d, c, a, s, w = (cfg[x] for x in ("B", "Hkv", "d", "c", "a", "s", "w"))
+    r = synth.rng(cfg["seed"] + 100)
+    tok = torch.from_numpy(synth.token_ids_iid(r, (B, P), cfg["vocab"], sep, cfg["p_sep"])).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(cfg["seed"] + 100)
+    k = torch.randn((B, Hkv, P, d), device=dev, generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, P, d), device=dev, generator=gen).to(torch.bfloat16)
+    idx = sa.build_index(tok, sep, a, 64)
+    cache = sa.SepCache(B, Hkv, d, c, a, s, w, device=dev)
+    for _ in range(3):
+        cache.prefill(k, v, tok, idx)
+    ev = Events()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.new(2)
+    torch.cuda.synchronize()
+    ev.record(e0, stream)
+    for _ in range(reps):
+        cache.prefill(k, v, tok, idx)
+    ev.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / reps
+    ev.close()
+    L = int(cache.state[:, :3].sum())
+    moved = L * Hkv * d * 2 * 2 * 2 + B * c * 4 * 2
+    del k, v
+    return dict(prompt_tokens=P, sequences=B, cached_slots_total=L, us_per_call=round(ms * 1e3, 3),
+                GBps=round(moved / (ms * 1e-3) / 1e9, 1))
 
 
 def cpu_leg(args, inp, E_seqs):

@@ -211,6 +211,21 @@ int sepcache_init(const sepcache* cache, void* stream);
 int sepcache_update(const sepcache* cache, const void* k_new, const void* v_new,
                     const int32_t* tok_new, const int32_t* sep_ids, int n_sep, void* stream);
 
+/* Prefill -> SepCache hand-off: sets every cache to what P calls of
+ * sepcache_update with the prompt's tokens (after sepcache_init) would leave,
+ * in one pass (the four blocks: beiduofen.top, "SepLLM's Architecture:
+ * Composing Efficiency"; capacities: atlas.scime.ai, "Measured effects
+ * reported in the paper").  k/v [B, Hkv, P, d] bf16 prompt rows (no rotary
+ * embedding), tok [B, P] int32 device; idx = sepattn_build_index of tok with
+ * the separator set the cache's later updates use and idx->a == cache->a (its
+ * window n is not used).  Rows are copied bit for bit; pos/tok are written for
+ * every slot and the counters set; earlier cache contents do not matter.
+ * Work: one short recurrence per sequence (one step per compression until the
+ * Separator block is full, then a closed form) and a copy of at most c - 1
+ * rows.  EINVAL on null pointers, P < 1 or an index of another shape or `a`. */
+int sepcache_prefill(const sepcache* cache, const void* k, const void* v, const int32_t* tok, int P,
+                     const sepattn_index* idx, void* stream);
+
 /* Device workspace bytes sepcache_decode needs for Hq query heads. */
 size_t sepcache_decode_workspace(const sepcache* cache, int Hq);
 

@@ -57,7 +57,7 @@ class _Cache(ctypes.Structure):
 EXPORTS = ["sepattn_strerror", "sepattn_index_bytes", "sepattn_index_bind", "sepattn_build_index",
            "sepattn_build_index_interval",
            "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepattn_bwd_profiled",
-           "sepcache_init", "sepcache_update",
+           "sepcache_init", "sepcache_update", "sepcache_prefill",
            "sepcache_decode_workspace", "sepcache_decode", "sepcache_decode_profiled",
            "sepattn_rope_table_host"]
 
@@ -96,6 +96,8 @@ def load_library(path=None):
                                        ctypes.POINTER(_Index), vp, vp, vp, vp, sz, vp, vp, i32]
     L.sepcache_init.restype = i32
     L.sepcache_init.argtypes = [ctypes.POINTER(_Cache), vp]
+    L.sepcache_prefill.restype = i32
+    L.sepcache_prefill.argtypes = [ctypes.POINTER(_Cache), vp, vp, vp, i32, ctypes.POINTER(_Index), vp]
     L.sepcache_update.restype = i32
     L.sepcache_update.argtypes = [ctypes.POINTER(_Cache), vp, vp, vp, vp, i32, vp]
     L.sepcache_decode_workspace.restype = sz
@@ -299,6 +301,17 @@ class SepCache:
         ids, ids_p = _host_ids(sep_ids)
         _check(load_library().sepcache_update(ctypes.byref(self.st), _ptr(k_new), _ptr(v_new), _ptr(tok_new),
                                               ids_p, len(ids), _stream()), "sepcache_update")
+
+    def prefill(self, k, v, tok, index):
+        """Set the caches to what streaming the prompt ``tok`` [B,P] (rows
+        k/v [B,Hkv,P,d] bf16) through ``update`` would leave; ``index`` is
+        build_index(tok, sep_ids, a, n) with this cache's ``a``."""
+        _need(tok, "tok", torch.int32)
+        B, P = tok.shape
+        _need(k, "k", torch.bfloat16, (self.B, self.Hkv, P, self.d))
+        _need(v, "v", torch.bfloat16, (self.B, self.Hkv, P, self.d))
+        _check(load_library().sepcache_prefill(ctypes.byref(self.st), _ptr(k), _ptr(v), _ptr(tok), P,
+                                               ctypes.byref(index.st), _stream()), "sepcache_prefill")
 
     def workspace_bytes(self, Hq):
         return load_library().sepcache_decode_workspace(ctypes.byref(self.st), Hq)

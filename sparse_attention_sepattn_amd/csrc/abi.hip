@@ -199,6 +199,17 @@ int sepcache_update(const sepcache* cache, const void* k_new, const void* v_new,
   return to_status(launch_cache_update(*cache, k_new, v_new, tok_new, sep, (hipStream_t)stream));
 }
 
+int sepcache_prefill(const sepcache* cache, const void* k, const void* v, const int32_t* tok, int P,
+                     const sepattn_index* idx, void* stream) {
+  int st = check_cache(cache);
+  if (st != SEPATTN_OK) return st;
+  if (!k || !v || !tok || !idx || P < 1) return SEPATTN_EINVAL;
+  if (idx->B != cache->B || idx->S != P || idx->a != cache->a || !idx->sep_prefix || !idx->anchor_pos)
+    return SEPATTN_EINVAL;
+  forget_stale_error();
+  return to_status(launch_cache_prefill(*cache, k, v, tok, P, *idx, (hipStream_t)stream));
+}
+
 size_t sepcache_decode_workspace(const sepcache* cache, int Hq) {
   if (check_cache(cache) != SEPATTN_OK || Hq < 1 || Hq % cache->Hkv != 0) return 0;
   return decode_workspace_bytes(*cache, Hq);

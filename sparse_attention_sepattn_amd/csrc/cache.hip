@@ -208,6 +208,111 @@ __global__ void __launch_bounds__(kUpdThreads) cache_update_kernel(UpdArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill -> SepCache hand-off: the cache each sequence would hold after its
+// P prompt tokens were streamed through the update above, built from the
+// prompt's index (separator prefix counts from position a and the anchor
+// list: initial tokens, then the separators in stream order).
+//
+// The Initial block is the first min(a, P) tokens; the Window is a suffix
+// [ws, P) of the stream; the Separator block holds the last Sp separators
+// before ws, Sp = min(s, #separators in [a, ws)).  With Sp separators held,
+// usage reaches c when the Window holds c - a - Sp tokens, and the compression
+// keeps the w newest, so ws advances by c - a - w - Sp (>= 1 since c > a+s+w);
+// once Sp = s the step is constant and the rest is one division.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_plan_kernel(int B, int P, int a, int s, int w, int c,
+                                                           const int32_t* __restrict__ sep_prefix,
+                                                           int32_t* __restrict__ state) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int32_t* pre = sep_prefix + (size_t)b * (P + 1);
+  int n_init, sp = 0, ws;
+  if (P <= a) {
+    n_init = P;
+    ws = P;
+  } else {
+    n_init = a;
+    ws = a;
+    while (true) {
+      if (sp == s) {
+        const long step = (long)c - a - w - s;
+        const long first = (long)ws + (c - a - s) - 1;  // the token whose append fills the cache
+        if (first <= P - 1) ws += (int)(((P - 1 - first) / step + 1) * step);
+        break;
+      }
+      const long t = (long)ws + (c - a - sp) - 1;
+      if (t > P - 1) break;
+      ws += c - a - sp - w;  // now <= P - w, so pre[ws] is in range
+      sp = min(s, pre[ws]);
+    }
+  }
+  int32_t* st = state + b * 4;
+  st[0] = n_init;
+  st[1] = sp;
+  st[2] = P - ws;
+  st[3] = P;
+}
+
+constexpr int kPrefillSlots = 16;  // cache slots per copy workgroup
+
+// Rows of the planned slots copied bit for bit; pos/tok written for every slot
+// (-1 past the occupied ones).
+__global__ void __launch_bounds__(256) prefill_copy_kernel(sepcache cache, const uint16_t* __restrict__ kin,
+                                                           const uint16_t* __restrict__ vin,
+                                                           const int32_t* __restrict__ tok_in, int P,
+                                                           const int32_t* __restrict__ sep_prefix,
+                                                           const int32_t* __restrict__ anchor_pos) {
+  const int b = blockIdx.y;
+  const int k0 = blockIdx.x * kPrefillSlots;
+  const int32_t* st = cache.state + b * 4;
+  const int n_init = st[0], sp = st[1], n_win = st[2];
+  const int L = n_init + sp + n_win;
+  const int ws = P - n_win;
+  const int cnt = sep_prefix[(size_t)b * (P + 1) + ws];  // separators in [a, ws)
+  const int a0 = min(cache.a, P);                          // separators start here in the anchor list
+  __shared__ int src_sh[kPrefillSlots];
+  if (threadIdx.x < kPrefillSlots) {
+    const int k = k0 + threadIdx.x;
+    int src = -1;
+    if (k < L) {
+      if (k < n_init) src = k;
+      else if (k < n_init + sp) src = anchor_pos[(size_t)b * P + a0 + (cnt - sp) + (k - n_init)];
+      else src = ws + (k - n_init - sp);
+    }
+    src_sh[threadIdx.x] = src;
+    if (k < cache.c) {
+      cache.pos[(size_t)b * cache.c + k] = src;
+      cache.tok[(size_t)b * cache.c + k] = src >= 0 ? tok_in[(size_t)b * P + src] : -1;
+    }
+  }
+  __syncthreads();
+  const int cpr = cache.d / 8;  // 16-byte chunks per row
+  const int per_slot = cache.Hkv * cpr;
+  for (int u = threadIdx.x; u < kPrefillSlots * per_slot; u += 256) {
+    const int sl = u / per_slot;
+    const int r = u - sl * per_slot;
+    const int h = r / cpr, ch = r - h * cpr;
+    const int src = src_sh[sl];
+    if (src < 0) continue;
+    const size_t in = (((size_t)b * cache.Hkv + h) * P + src) * cache.d + 8 * ch;
+    const size_t out = (((size_t)b * cache.Hkv + h) * cache.c + (k0 + sl)) * cache.d + 8 * ch;
+    *(u32x4*)((uint16_t*)cache.k + out) = *(const u32x4*)(kin + in);
+    *(u32x4*)((uint16_t*)cache.v + out) = *(const u32x4*)(vin + in);
+  }
+}
+
+hipError_t launch_cache_prefill(const sepcache& c, const void* k, const void* v, const int32_t* tok, int P,
+                                const sepattn_index& idx, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3((c.B + 255) / 256), dim3(256), 0, stream, c.B, P, c.a, c.s, c.w,
+                     c.c, idx.sep_prefix, c.state);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_copy_kernel, dim3((c.c + kPrefillSlots - 1) / kPrefillSlots, c.B), dim3(256), 0,
+                     stream, c, (const uint16_t*)k, (const uint16_t*)v, tok, P, idx.sep_prefix, idx.anchor_pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_init(const sepcache& c, hipStream_t stream) {
   hipLaunchKernelGGL(cache_init_kernel, dim3(c.B), dim3(256), 0, stream, c.c, c.pos, c.tok, c.state);
   return hipGetLastError();

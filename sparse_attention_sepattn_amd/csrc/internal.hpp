@@ -33,6 +33,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       void* dk, void* dv, void* ws, hipStream_t stream, hipEvent_t* ev);
 
 hipError_t launch_cache_init(const sepcache& c, hipStream_t stream);
+hipError_t launch_cache_prefill(const sepcache& c, const void* k, const void* v, const int32_t* tok, int P,
+                                const sepattn_index& idx, hipStream_t stream);
 hipError_t launch_cache_update(const sepcache& c, const void* k_new, const void* v_new,
                                const int32_t* tok_new, const SepSet& sep, hipStream_t stream);
 size_t decode_workspace_bytes(const sepcache& c, int Hq);

@@ -98,6 +98,18 @@ def test_cache_capacity_errors():
     assert L.sepcache_init(ctypes.byref(c), z) == 3          # w < 1
     c.w, c.d = 256, 96
     assert L.sepcache_init(ctypes.byref(c), z) == 2          # head dim
+    # prefill hand-off: index of another shape or another `a`, P < 1 (all
+    # rejected on the host before any launch)
+    c.d = 128
+    st = sa._Index()
+    L.sepattn_index_bind(ctypes.c_void_p(fake), L.sepattn_index_bytes(2, 64), 2, 64, ctypes.byref(st))
+    st.a, st.n = 4, 64
+    f = ctypes.c_void_p(fake)
+    assert L.sepcache_prefill(ctypes.byref(c), f, f, f, 32, ctypes.byref(st), z) == 1       # P != idx.S
+    st.a = 3
+    assert L.sepcache_prefill(ctypes.byref(c), f, f, f, 64, ctypes.byref(st), z) == 1       # a mismatch
+    st.a = 4
+    assert L.sepcache_prefill(ctypes.byref(c), f, f, f, 0, ctypes.byref(st), z) == 1        # P < 1
     c.d = 128
     assert L.sepcache_decode_workspace(ctypes.byref(c), 32) > 0
     assert L.sepcache_decode_workspace(ctypes.byref(c), 30) == 0   # Hq % Hkv
