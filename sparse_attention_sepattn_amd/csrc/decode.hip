@@ -11,6 +11,12 @@
 // step and shared by the query heads of its group.  The slots are split into
 // chunks of kDecChunk; one workgroup per (chunk, kv head, sequence) writes an
 // unnormalised partial (max, sum, o) and a second kernel merges the chunks.
+// Every load of a chunk is issued up front, unconditionally (rows past the
+// chunk are clamped to its last row and never used, so no branch splits the
+// loads and no wait lands between them), query first, then K pass by pass,
+// then V; the rotary angles of later passes come from one angle addition
+// per pass.  Cross-lane sums and maxima stay in registers (DPP, ds_swizzle,
+// v_permlane32_swap).
 #include "internal.hpp"
 
 namespace sepattn {
@@ -42,17 +48,81 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4& x, float* f) {
   }
 }
 
+
+// Cross-lane reductions in registers (no LDS round trip):
+//   DPP quad_perm [1,0,3,2] / [2,3,0,1] exchange with lane ^ 1 / lane ^ 2;
+//   DPP row_ror:4 / row_ror:8 rotate within each 16-lane row;
+//   ds_swizzle in bit mode (and 0x1f, xor 0x10) exchanges with lane ^ 16;
+//   v_permlane32_swap exchanges the two 32-lane halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+__device__ __forceinline__ float swz_xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float swz_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+// sum / max of a lane and lane ^ 32 (v_permlane32_swap of (x, x) gives the
+// lower half's values in both halves and the upper half's in both halves)
+__device__ __forceinline__ float halves_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// sum over each aligned group of N lanes (N = 4 or 8), in every lane
+template <int N>
+__device__ __forceinline__ float group_sum(float a) {
+  a += dpp<kQuadXor1>(a);
+  a += dpp<kQuadXor2>(a);
+  if constexpr (N == 8) a += swz_xor4(a);
+  return a;
+}
+// all-lane sum / max over the wave: after the quad steps, row_ror:4 and then
+// row_ror:8 add the other three quads of the row (whichever way the rotation
+// runs), then the rows and the halves
+__device__ __forceinline__ float wave_sum(float a) {
+  a += dpp<kQuadXor1>(a);
+  a += dpp<kQuadXor2>(a);
+  a += dpp<kRowRor4>(a);
+  a += dpp<kRowRor8>(a);
+  a += swz_xor16(a);
+  return halves_sum(a);
+}
+__device__ __forceinline__ float wave_max(float a) {
+  a = fmaxf(a, dpp<kQuadXor1>(a));
+  a = fmaxf(a, dpp<kQuadXor2>(a));
+  a = fmaxf(a, dpp<kRowRor4>(a));
+  a = fmaxf(a, dpp<kRowRor8>(a));
+  a = fmaxf(a, swz_xor16(a));
+  return halves_max(a);
+}
+
+#ifndef SEPATTN_DEC_OCC
+#define SEPATTN_DEC_OCC 2
+#endif
 template <int D, int G>
-__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecArgs p) {
+__global__ void __launch_bounds__(kDecThreads, SEPATTN_DEC_OCC) decode_kernel(DecArgs p) {
   constexpr int H2 = D / 2;
-  constexpr int LPS = D / 16;             // lanes per slot in the score phase
-  constexpr int SPP = kDecThreads / LPS;  // slots per pass
+  constexpr int LPS = D / 16;             // lanes per slot in the score phase (8 rotary pairs each)
+  constexpr int SPP = kDecThreads / LPS;  // slots per score pass
+  constexpr int NPASS = kDecChunk / SPP;  // score passes per chunk
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int NSG = kDecThreads / CPR;  // slot groups in the P V phase
+  constexpr int VPT = kDecChunk / NSG;    // value rows per thread
+  constexpr int SGW = kWave / CPR;        // slot groups per wave
+  constexpr int NW = kDecThreads / kWave;
 
-  __shared__ float qs[G][D];
+  __shared__ __attribute__((aligned(16))) float qs[G][D];
   __shared__ float sc[G][kDecChunk];
-  __shared__ float red[NSG][G][D];
+  __shared__ __attribute__((aligned(16))) float red[NW][G][D];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -70,83 +140,129 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecArgs p) {
     return;
   }
   const int ns = min(kDecChunk, L - s0);
-
-  // rotate the query at slot L-1
-  for (int u = tid; u < G * H2; u += kDecThreads) {
-    const int hg = u / H2, m = u - hg * H2;
-    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + g * G + hg) * D;
-    const float xl = bf16_bits_to_f32(qrow[m]), xh = bf16_bits_to_f32(qrow[m + H2]);
-    const float cs = p.cos[(size_t)(L - 1) * H2 + m], sn = p.sin[(size_t)(L - 1) * H2 + m];
-    qs[hg][m] = xl * cs - xh * sn;
-    qs[hg][m + H2] = xh * cs + xl * sn;
-  }
-  __syncthreads();
-
   const uint16_t* Kb = p.k + (((size_t)b * p.Hkv + g) * p.c) * D;
   const uint16_t* Vb = p.v + (((size_t)b * p.Hkv + g) * p.c) * D;
 
-  // scores: LPS lanes per slot, each rotating 8 (lo, hi) pairs
+  // Loads are issued in the order they are consumed (query and its rotary
+  // row, K pass by pass, then V): a wait for one load is a wait for every
+  // load issued before it, so each phase only waits for its own data.
+  constexpr int QPT = (G * H2 + kDecThreads - 1) / kDecThreads;  // query pairs per thread
+  uint16_t xlb[QPT], xhb[QPT];  // raw bf16: converted after every load is out
+  float qc[QPT], qsn[QPT];
+#pragma unroll
+  for (int r = 0; r < QPT; ++r) {
+    const int u = min(tid + r * kDecThreads, G * H2 - 1);  // clamped: every load unconditional
+    const int hg = u / H2, m = u - hg * H2;
+    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + g * G + hg) * D;
+    xlb[r] = qrow[m];
+    xhb[r] = qrow[m + H2];
+    qc[r] = p.cos[(size_t)(L - 1) * H2 + m];
+    qsn[r] = p.sin[(size_t)(L - 1) * H2 + m];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the query's loads go out first
+  // rotary angles of this lane's 8 frequencies at its first slot, and the
+  // rotation by SPP slots that carries them to the next pass (angle addition)
+  const int sub = tid % LPS, sl = tid / LPS;
+  f32x4 cs[2], sn[2], cstep[2], sstep[2];
   {
-    const int sub = tid % LPS, sl = tid / LPS;
-    for (int base = 0; base < ns; base += SPP) {
-      const int j = base + sl;
-      float acc[G];
+    const int slot0 = s0 + sl < L ? s0 + sl : L - 1;
 #pragma unroll
-      for (int hg = 0; hg < G; ++hg) acc[hg] = 0.f;
-      if (j < ns) {
-        const int slot = s0 + j;
-        float kl[8], kh[8];
-        bf16x8_to_f32(*(const u32x4*)(Kb + (size_t)slot * D + 8 * sub), kl);
-        bf16x8_to_f32(*(const u32x4*)(Kb + (size_t)slot * D + H2 + 8 * sub), kh);
-        const f32x4 c0 = *(const f32x4*)(p.cos + (size_t)slot * H2 + 8 * sub);
-        const f32x4 c1 = *(const f32x4*)(p.cos + (size_t)slot * H2 + 8 * sub + 4);
-        const f32x4 s0v = *(const f32x4*)(p.sin + (size_t)slot * H2 + 8 * sub);
-        const f32x4 s1v = *(const f32x4*)(p.sin + (size_t)slot * H2 + 8 * sub + 4);
-        float rl[8], rh[8];
+    for (int h = 0; h < 2; ++h) {
+      cs[h] = *(const f32x4*)(p.cos + (size_t)slot0 * H2 + 8 * sub + 4 * h);
+      sn[h] = *(const f32x4*)(p.sin + (size_t)slot0 * H2 + 8 * sub + 4 * h);
+      // table row SPP exists whenever it is used (ns > SPP implies c > SPP);
+      // the row index is clamped so the load is unconditional
+      const int srow = min(SPP, p.c - 1);
+      cstep[h] = *(const f32x4*)(p.cos + (size_t)srow * H2 + 8 * sub + 4 * h);
+      sstep[h] = *(const f32x4*)(p.sin + (size_t)srow * H2 + 8 * sub + 4 * h);
+    }
+  }
+  // rows past the chunk are clamped to its last row (loaded, never used)
+  u32x4 klo[NPASS], khi[NPASS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cs = e < 4 ? c0[e] : c1[e - 4];
-          const float sn = e < 4 ? s0v[e] : s1v[e - 4];
-          rl[e] = kl[e] * cs - kh[e] * sn;
-          rh[e] = kh[e] * cs + kl[e] * sn;
-        }
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int j = min(ps * SPP + sl, ns - 1);
+    klo[ps] = *(const u32x4*)(Kb + (size_t)(s0 + j) * D + 8 * sub);
+    khi[ps] = *(const u32x4*)(Kb + (size_t)(s0 + j) * D + H2 + 8 * sub);
+  }
+  const int cc = tid % CPR, sg = tid / CPR;
+  u32x4 vr[VPT];
 #pragma unroll
-        for (int hg = 0; hg < G; ++hg) {
-          float a = 0.f;
+  for (int k = 0; k < VPT; ++k) {
+    const int j = min(sg + NSG * k, ns - 1);
+    vr[k] = *(const u32x4*)(Vb + (size_t)(s0 + j) * D + 8 * cc);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load is in flight before the first use
+
+  // the query of each head of the group, rotated at slot L-1
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a += qs[hg][8 * sub + e] * rl[e] + qs[hg][H2 + 8 * sub + e] * rh[e];
-          acc[hg] = a;
-        }
+  for (int r = 0; r < QPT; ++r) {
+    // clamped like the loads: extra threads rewrite the last pair with the same value
+    const int u = min(tid + r * kDecThreads, G * H2 - 1);
+    const int hg = u / H2, m = u - hg * H2;
+    const float xl = bf16_bits_to_f32(xlb[r]), xh = bf16_bits_to_f32(xhb[r]);
+    qs[hg][m] = xl * qc[r] - xh * qsn[r];
+    qs[hg][m + H2] = xh * qc[r] + xl * qsn[r];
+  }
+  __syncthreads();
+
+  // ---- scores: LPS lanes per slot, each rotating 8 (lo, hi) pairs ----
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    float kl[8], kh[8];
+    bf16x8_to_f32(klo[ps], kl);
+    bf16x8_to_f32(khi[ps], kh);
+    float rl[8], rh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c1 = cs[e >> 2][e & 3], s1 = sn[e >> 2][e & 3];
+      rl[e] = kl[e] * c1 - kh[e] * s1;
+      rh[e] = kh[e] * c1 + kl[e] * s1;
+    }
+    float acc[G];
+#pragma unroll
+    for (int hg = 0; hg < G; ++hg) {
+      const f32x4 ql0 = *(const f32x4*)&qs[hg][8 * sub], ql1 = *(const f32x4*)&qs[hg][8 * sub + 4];
+      const f32x4 qh0 = *(const f32x4*)&qs[hg][H2 + 8 * sub], qh1 = *(const f32x4*)&qs[hg][H2 + 8 * sub + 4];
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a += ql0[e] * rl[e] + qh0[e] * rh[e];
+        a += ql1[e] * rl[4 + e] + qh1[e] * rh[4 + e];
       }
+      a = group_sum<LPS>(a);
+      acc[hg] = a;
+    }
+    const int j = ps * SPP + sl;
+    if (sub == 0 && j < ns) {
 #pragma unroll
-      for (int hg = 0; hg < G; ++hg) {
+      for (int hg = 0; hg < G; ++hg) sc[hg][j] = acc[hg] * p.scale_log2;
+    }
+    if (ps + 1 < NPASS) {
 #pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) acc[hg] += __shfl_xor(acc[hg], off, 64);
-      }
-      if (sub == 0 && j < ns) {
-#pragma unroll
-        for (int hg = 0; hg < G; ++hg) sc[hg][j] = acc[hg] * p.scale_log2;
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 c0 = cs[h], sv = sn[h];
+        cs[h] = c0 * cstep[h] - sv * sstep[h];
+        sn[h] = sv * cstep[h] + c0 * sstep[h];
       }
     }
   }
   __syncthreads();
 
-  // chunk softmax per head: one wave per head (G <= 8 heads over 4 waves)
+  // ---- chunk softmax per head (waves take heads in turn) ----
   {
     const int lane = tid & 63, wv = tid >> 6;
-    for (int hg = wv; hg < G; hg += kDecThreads / 64) {
+    for (int hg = wv; hg < G; hg += NW) {
       float mx = -INFINITY;
-      for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, sc[hg][j]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      for (int j = lane; j < ns; j += kWave) mx = fmaxf(mx, sc[hg][j]);
+      mx = wave_max(mx);
       float sum = 0.f;
-      for (int j = lane; j < ns; j += 64) {
+      for (int j = lane; j < ns; j += kWave) {
         const float e = fast_exp2(sc[hg][j] - mx);
         sc[hg][j] = e;
         sum += e;
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      sum = wave_sum(sum);
       if (lane == 0) {
         part0[hg * part_stride + D] = mx;
         part0[hg * part_stride + D + 1] = sum;
@@ -155,17 +271,18 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecArgs p) {
   }
   __syncthreads();
 
-  // o = sum_j p_j V_j: thread (chunk cc, slot group sg)
-  {
-    const int cc = tid % CPR, sg = tid / CPR;
-    float acc[G][8];
+  // ---- o = sum_j p_j V_j from the value rows already in registers ----
+  float acc[G][8];
 #pragma unroll
-    for (int hg = 0; hg < G; ++hg)
+  for (int hg = 0; hg < G; ++hg)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hg][e] = 0.f;
-    for (int j = sg; j < ns; j += NSG) {
+    for (int e = 0; e < 8; ++e) acc[hg][e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int j = sg + NSG * k;
+    if (j < ns) {
       float vv[8];
-      bf16x8_to_f32(*(const u32x4*)(Vb + (size_t)(s0 + j) * D + 8 * cc), vv);
+      bf16x8_to_f32(vr[k], vv);
 #pragma unroll
       for (int hg = 0; hg < G; ++hg) {
         const float pj = sc[hg][j];
@@ -173,17 +290,34 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecArgs p) {
         for (int e = 0; e < 8; ++e) acc[hg][e] += pj * vv[e];
       }
     }
-#pragma unroll
-    for (int hg = 0; hg < G; ++hg)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[sg][hg][8 * cc + e] = acc[hg][e];
   }
+  // slot groups of one wave (lanes cc, cc + CPR, ...) in registers, then the
+  // waves through LDS
+#pragma unroll
+  for (int hg = 0; hg < G; ++hg)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = acc[hg][e];
+      if constexpr (CPR == 8) a += dpp<kRowRor8>(a);  // lane ^ 8 (a rotation by 8 of 16 lanes)
+      a += swz_xor16(a);
+      a = halves_sum(a);
+      acc[hg][e] = a;
+    }
+  const int lane = tid & 63, wv = tid >> 6;
+  if (lane < CPR) {
+#pragma unroll
+    for (int hg = 0; hg < G; ++hg) {
+      *(f32x4*)&red[wv][hg][8 * cc] = f32x4{acc[hg][0], acc[hg][1], acc[hg][2], acc[hg][3]};
+      *(f32x4*)&red[wv][hg][8 * cc + 4] = f32x4{acc[hg][4], acc[hg][5], acc[hg][6], acc[hg][7]};
+    }
+  }
+  static_assert(SGW * CPR == kWave, "slot groups must tile a wave");
   __syncthreads();
   for (int u = tid; u < G * D; u += kDecThreads) {
     const int hg = u / D, dd = u - hg * D;
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < NSG; ++k) s += red[k][hg][dd];
+    for (int k = 0; k < NW; ++k) s += red[k][hg][dd];
     part0[hg * part_stride + dd] = s;
   }
 }
