@@ -49,6 +49,9 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_DKDV_PREFETCH
 #define SEPATTN_DKDV_PREFETCH 1
 #endif
+#ifndef SEPATTN_DKDV_DMA
+#define SEPATTN_DKDV_DMA 1  // dK/dV items: Q/dO tiles and LSE/D loaded straight into LDS
+#endif
 #ifndef SEPATTN_DQ_DMA
 #define SEPATTN_DQ_DMA 1  // dQ: K/V tiles loaded straight into LDS
 #endif
@@ -74,6 +77,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* Dvec;  // [B,Hq,S]
+  float* LD;    // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then D (zero past S)
   float* dKa;   // [nchunk+1,B,Hkv,S,D] fp32 partials by slot and anchor index
   float* dVa;
   const uint8_t* is_sep;
@@ -81,6 +85,7 @@ struct BwdArgs {
   const int32_t* anchor_pos;
   const int32_t* qtile;
   int B, Hq, Hkv, S, a, n, QT;
+  int SB;                   // ceil(S / 64) row blocks of LD
   int nchunk, chunk_tiles;  // anchor work split: nchunk chunks of chunk_tiles query tiles
   int units;                // ceil(S / 128) key units per (sequence, kv head)
   int anchor_lanes;         // anchor work items per (sequence, kv head, chunk); each walks units
@@ -122,10 +127,16 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
   constexpr int VEC = Traits<T>::VEC;
   constexpr int TPR = D / VEC;  // threads per row
-  const size_t rows = (size_t)p.B * p.Hq * p.S;
-  const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  // rows of the 64-padded blocks of every (sequence, head)
+  const size_t rows_pad = (size_t)p.B * p.Hq * p.SB * kKTile;
+  const size_t prow = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int sub = threadIdx.x % TPR;
-  if (row >= rows) return;
+  if (prow >= rows_pad) return;
+  const size_t per_bh = (size_t)p.SB * kKTile;
+  const size_t bh = prow / per_bh;
+  const int r = (int)(prow - bh * per_bh);
+  const bool valid = r < p.S;
+  const size_t row = bh * p.S + (valid ? r : 0);
   float acc = 0.f;
   const T* orow = (const T*)p.o + row * D + sub * VEC;
   const T* grow = (const T*)p.dout + row * D + sub * VEC;
@@ -143,7 +154,14 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (sub == 0) p.Dvec[row] = acc;
+  if (sub == 0) {
+    const float lse2 = valid ? p.lse[row] * 1.4426950408889634f : 0.f;
+    acc = valid ? acc : 0.f;
+    if (valid) p.Dvec[row] = acc;
+    float* blk = p.LD + (bh * p.SB + r / kKTile) * (2 * kKTile);
+    blk[r % kKTile] = lse2;
+    blk[kKTile + r % kKTile] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -151,7 +169,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool ANCHOR>
 __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk, T* Qs, T* dOs,
-                                          float* lse_s, float* dd_s) {
+                                          float* ld_s) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kBwdThreads> Regs;
@@ -161,7 +179,9 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   constexpr int NF = D / KSTEP;    // K/V fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of dK^T / dV^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps over one 32-query block
-  constexpr int PF = bwd_prefetch<T, D, true>();
+  constexpr bool kDMA = SEPATTN_DKDV_DMA;  // Q/dO tiles and LSE/D go global -> LDS directly
+  constexpr int PF = kDMA ? 1 : bwd_prefetch<T, D, true>();
+  typedef TileDMA<T, D, kBwdThreads> DMA;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -212,18 +232,33 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     const int r = it % (2 * n_q);
     return (qi_begin + (r >> 1)) * kQTile + (r & 1) * kKTile;
   };
+  const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
+  const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
   auto issue = [&](int it, Regs& rq, Regs& ro, float& pl, float& pd) {
     const int h = it_head(it);
     const int r0 = it_row0(it);
+    const size_t bh = (size_t)b * p.Hq + h;
     int rows[Regs::NU];
     Regs::rows(rows, RowSrc{nullptr, r0, p.S}, tid);
-    rq.issue((const T*)p.q + (((size_t)b * p.Hq + h) * p.S) * D, rows, tid);
-    ro.issue((const T*)p.dout + (((size_t)b * p.Hq + h) * p.S) * D, rows, tid);
-    if (tid < kKTile) {
-      const int r = r0 + tid;
-      const size_t o = ((size_t)b * p.Hq + h) * p.S + r;
-      pl = r < p.S ? p.lse[o] * 1.4426950408889634f : 0.f;
-      pd = r < p.S ? p.Dvec[o] : 0.f;
+    if constexpr (kDMA) {
+      DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, Qs + (it & 1) * G::ELEMS, tid);
+      DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, dOs + (it & 1) * G::ELEMS,
+                 tid);
+      // this wave's own copy of the tile's 64 (log2(e)*LSE, D) pairs: lanes
+      // 0..31 carry the 512-byte block, lanes 32..63 read past the buffer
+      // (zeros into the unused half of the wave's 1 KB slot)
+      const unsigned off = lane < 32 ? (unsigned)((r0 / kKTile) * 2 * kKTile * 4 + lane * 16) : ldbytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(p.LD + bh * p.SB * 2 * kKTile, ldbytes),
+                                               (__attribute__((address_space(3))) void*)(ld_s + ((it & 1) * 4 + w) * 256),
+                                               16, off, 0, 0, 0);
+    } else {
+      rq.issue((const T*)p.q + bh * p.S * D, rows, tid);
+      ro.issue((const T*)p.dout + bh * p.S * D, rows, tid);
+      if (tid < kKTile) {
+        const float* blk = p.LD + (bh * p.SB + r0 / kKTile) * 2 * kKTile;
+        pl = blk[tid];
+        pd = blk[kKTile + tid];
+      }
     }
   };
 
@@ -232,15 +267,15 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   if (n_it > 0) issue(0, rqA, roA, plA, pdA);
   if (PF == 2 && n_it > 1) issue(1, rqB, roB, plB, pdB);
 
+  // this lane's key rows (a lane without a key reads row 0: its column is
+  // masked out of every tile and never stored)
   frag kf[NF], vf[NF];
+  {
+    const int kr = krow >= 0 ? krow : 0;
 #pragma unroll
-  for (int c = 0; c < NF; ++c) {
-    if (krow >= 0) {
-      kf[c] = *(const frag*)(Kg + (size_t)krow * D + c * KSTEP + EPL * hh);
-      vf[c] = *(const frag*)(Vg + (size_t)krow * D + c * KSTEP + EPL * hh);
-    } else {
-      kf[c] = frag{};
-      vf[c] = frag{};
+    for (int c = 0; c < NF; ++c) {
+      kf[c] = *(const frag*)(Kg + (size_t)kr * D + c * KSTEP + EPL * hh);
+      vf[c] = *(const frag*)(Vg + (size_t)kr * D + c * KSTEP + EPL * hh);
     }
   }
 
@@ -255,13 +290,17 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     const int buf = it & 1;
     T* Qb = Qs + buf * G::ELEMS;
     T* dOb = dOs + buf * G::ELEMS;
-    float* lb = lse_s + buf * kKTile;
-    float* db_ = dd_s + buf * kKTile;
-    rq.store(Qb, tid);
-    ro.store(dOb, tid);
-    if (tid < kKTile) {
-      lb[tid] = pl;
-      db_[tid] = pd;
+    float* lb = ld_s + (buf * 4 + (kDMA ? w : 0)) * 256;  // log2(e)*LSE of the tile's 64 rows
+    float* db_ = lb + kKTile;                                 // then D
+    if constexpr (!kDMA) {
+      rq.store(Qb, tid);
+      ro.store(dOb, tid);
+      if (tid < kKTile) {
+        lb[tid] = pl;
+        db_[tid] = pd;
+      }
+    } else {
+      wait_vm_all();  // this wave's part of tile `it` (and its LSE/D copy) has landed in LDS
     }
     __syncthreads();  // tile `it` visible; every wave is done with tile it-1's buffer
     const int r0 = it_row0(it);
@@ -665,8 +704,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   typedef TileGeom<T, D> G;
   __shared__ __attribute__((aligned(16))) T smA[2 * G::ELEMS];
   __shared__ __attribute__((aligned(16))) T smB[2 * G::ELEMS];
-  __shared__ __attribute__((aligned(16))) float smL[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) float smD[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) float smLD[2 * 4 * 256];  // [buffer][wave][LSE x 64, D x 64, spare]
 
   int x = blockIdx.x;
   const int BG = p.B * p.Hkv;
@@ -678,7 +716,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
     const int bg = r / p.nchunk;
     const int chunk = r - bg * p.nchunk;
     for (int unit = lane0; unit < p.units; unit += p.anchor_lanes) {
-      if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smL, smD)) break;
+      if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smLD)) break;
       __syncthreads();  // the next unit refills the tile buffers
     }
     return;
@@ -696,7 +734,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   const int li = xcd_local_index(blockIdx.x, p.n_anchor_items + p.n_dq_items, p.n_band_items);
   const int bg = li / p.units;
   const int unit = li - bg * p.units;
-  dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, smA, smB, smL, smD);
+  dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, smA, smB, smLD);
 }
 
 // ---------------------------------------------------------------------------
@@ -737,13 +775,15 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   const int QT = (S + kQTile - 1) / kQTile;
   int nchunk, ct;
   anchor_split(B, Hkv, S, QT, &nchunk, &ct);
-  return a256((size_t)B * Hq * S * 4) + 2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
+  const size_t SB = (S + kKTile - 1) / kKTile;
+  return a256((size_t)B * Hq * S * 4) + a256((size_t)B * Hq * SB * 2 * kKTile * 4) +
+         2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
 }
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   constexpr int TPR = D / Traits<T>::VEC;
-  const size_t rows = (size_t)a.B * a.Hq * a.S;
+  const size_t rows = (size_t)a.B * a.Hq * a.SB * kKTile;  // 64-padded rows
   const int pre_blocks = (int)((rows + (256 / TPR) - 1) / (256 / TPR));
   const int main_blocks = a.n_anchor_items + a.n_dq_items + a.n_band_items;
   const int fin_rows_per_block = 256 / (D / 4);
@@ -779,6 +819,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   char* w = (char*)ws;
   a.Dvec = (float*)w;
   w += a256((size_t)sh.B * sh.Hq * sh.S * 4);
+  a.SB = (sh.S + kKTile - 1) / kKTile;
+  a.LD = (float*)w;
+  w += a256((size_t)sh.B * sh.Hq * a.SB * 2 * kKTile * 4);
   a.QT = (sh.S + kQTile - 1) / kQTile;
   anchor_split(sh.B, sh.Hkv, sh.S, a.QT, &a.nchunk, &a.chunk_tiles);
   a.dKa = (float*)w;
