@@ -248,7 +248,48 @@ def prefill_leg(args, torch, sa, synth):
                       traffic=traffic, algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
                       avg_launch_ms=round(dom_ms, 5)),
     )
+    result["dense_layer"] = dense_layer(args, torch, sa, (q, k, v, do), tok, sep, scale, cfg, ev_cls=Events)
     return result, inp, E_seqs
+
+
+def dense_layer(args, torch, sa, tensors, tok, sep, scale, cfg, ev_cls):
+    """The same inputs with a window n = S: every earlier key visible (a dense
+    causal layer, as the hybrid's first and last layers), whole steps timed."""
+    q, k, v, do = tensors
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    a, n = cfg["a"], S
+    dev = q.device
+    idx = sa.Index(B, S, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(sa.bwd_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        sa.build_index(tok, sep, a, n, index=idx)
+        sa.fwd(q, k, v, idx, scale, o=o, lse=lse)
+        sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    ev = ev_cls()
+    stream = torch.cuda.current_stream().cuda_stream
+    t0, t1 = ev.new(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for _ in range(args.steps):
+        step()
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / args.steps
+    ev.close()
+    qt = idx.qtile.cpu().numpy().astype(np.int64)
+    E = int((qt[:, :, 5] * 64 * qt[:, :, 4]).sum()) * Hq
+    causal = B * Hq * S * (S + 1) // 2
+    return dict(workload=f"same shapes, window n = S = {S} (dense causal)", ms_per_step=round(ms, 4),
+                kept_tile_TFLOPs=round(14 * d * E / (ms * 1e-3) / 1e12, 3),
+                causal_TFLOPs=round(14 * d * causal / (ms * 1e-3) / 1e12, 3))
 
 
 def decode_leg(args, torch, sa, synth):
