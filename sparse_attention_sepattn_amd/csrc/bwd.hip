@@ -35,6 +35,7 @@ namespace sepattn {
 
 constexpr int kBwdThreads = 256;
 constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
+constexpr int kPreRows = 128;    // rows of D per workgroup of the pre kernel
 
 // Workgroups per CU the register budget targets, and how many tiles ahead
 // global loads are issued: the d=128 and fp32 kernels keep more operands
@@ -42,15 +43,21 @@ constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
 #ifndef SEPATTN_BWD_OCC
 #define SEPATTN_BWD_OCC 2
 #endif
+#ifndef SEPATTN_BWD_OCC128
+#define SEPATTN_BWD_OCC128 1
+#endif
 template <typename T, int D>
 constexpr int bwd_occupancy() {
-  return (sizeof(T) == 2 && D == 64) ? SEPATTN_BWD_OCC : 1;
+  return sizeof(T) == 2 ? (D == 64 ? SEPATTN_BWD_OCC : SEPATTN_BWD_OCC128) : 1;
 }
 #ifndef SEPATTN_DKDV_PREFETCH
 #define SEPATTN_DKDV_PREFETCH 1
 #endif
 #ifndef SEPATTN_DKDV_DMA
 #define SEPATTN_DKDV_DMA 1  // dK/dV items: Q/dO tiles and LSE/D loaded straight into LDS
+#endif
+#ifndef SEPATTN_FIN_BLOCKS
+#define SEPATTN_FIN_BLOCKS 1024  // finalize workgroups in all (before the per-(b, kv head) floor of one)
 #endif
 #ifndef SEPATTN_DQ_DMA
 #define SEPATTN_DQ_DMA 1  // dQ: K/V tiles loaded straight into LDS
@@ -126,41 +133,58 @@ __device__ __forceinline__ int anchor_slot(const BwdArgs& p, int b, int krow, bo
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
   constexpr int VEC = Traits<T>::VEC;
-  constexpr int TPR = D / VEC;  // threads per row
+  constexpr int TPR = D / VEC;       // threads per row
+  constexpr int RPP = 256 / TPR;     // rows per pass of the workgroup
+  constexpr int NR = kPreRows / RPP;  // rows per thread, all loads in flight together
   // rows of the 64-padded blocks of every (sequence, head)
   const size_t rows_pad = (size_t)p.B * p.Hq * p.SB * kKTile;
-  const size_t prow = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int sub = threadIdx.x % TPR;
-  if (prow >= rows_pad) return;
   const size_t per_bh = (size_t)p.SB * kKTile;
-  const size_t bh = prow / per_bh;
-  const int r = (int)(prow - bh * per_bh);
-  const bool valid = r < p.S;
-  const size_t row = bh * p.S + (valid ? r : 0);
-  float acc = 0.f;
-  const T* orow = (const T*)p.o + row * D + sub * VEC;
-  const T* grow = (const T*)p.dout + row * D + sub * VEC;
-  if constexpr (VEC == 8) {
-    const u32x4 a = *(const u32x4*)orow, b = *(const u32x4*)grow;
+  const int sub = threadIdx.x % TPR;
+  size_t prow[NR], row[NR];
+  bool valid[NR];
+  float acc[NR], lse[NR];
+  typedef typename std::conditional<VEC == 8, u32x4, f32x4>::type V4;
+  V4 ov[NR], gv[NR];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += __uint_as_float(a[w] << 16) * __uint_as_float(b[w] << 16);
-      acc += __uint_as_float(a[w] & 0xFFFF0000u) * __uint_as_float(b[w] & 0xFFFF0000u);
-    }
-  } else {
-    const f32x4 a = *(const f32x4*)orow, b = *(const f32x4*)grow;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc += a[e] * b[e];
+  for (int k = 0; k < NR; ++k) {
+    prow[k] = (size_t)blockIdx.x * kPreRows + k * RPP + threadIdx.x / TPR;
+    const size_t pr = prow[k] < rows_pad ? prow[k] : rows_pad - 1;
+    const size_t bh = pr / per_bh;
+    const int r = (int)(pr - bh * per_bh);
+    valid[k] = prow[k] < rows_pad && r < p.S;
+    row[k] = bh * p.S + (r < p.S ? r : 0);
+    ov[k] = *(const V4*)((const T*)p.o + row[k] * D + sub * VEC);
+    gv[k] = *(const V4*)((const T*)p.dout + row[k] * D + sub * VEC);
+    lse[k] = p.lse[row[k]];
   }
 #pragma unroll
-  for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (sub == 0) {
-    const float lse2 = valid ? p.lse[row] * 1.4426950408889634f : 0.f;
-    acc = valid ? acc : 0.f;
-    if (valid) p.Dvec[row] = acc;
+  for (int k = 0; k < NR; ++k) {
+    float a = 0.f;
+    if constexpr (VEC == 8) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a += __uint_as_float(ov[k][w] << 16) * __uint_as_float(gv[k][w] << 16);
+        a += __uint_as_float(ov[k][w] & 0xFFFF0000u) * __uint_as_float(gv[k][w] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a += ov[k][e] * gv[k][e];
+    }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) a += __shfl_xor(a, off, 64);
+    acc[k] = a;
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    if (sub != 0 || prow[k] >= rows_pad) continue;
+    const size_t bh = prow[k] / per_bh;
+    const int r = (int)(prow[k] - bh * per_bh);
+    const float lse2 = valid[k] ? lse[k] * 1.4426950408889634f : 0.f;
+    const float d = valid[k] ? acc[k] : 0.f;
+    if (valid[k]) p.Dvec[row[k]] = d;
     float* blk = p.LD + (bh * p.SB + r / kKTile) * (2 * kKTile);
     blk[r % kKTile] = lse2;
-    blk[kKTile + r % kKTile] = acc;
+    blk[kKTile + r % kKTile] = d;
   }
 }
 
@@ -746,24 +770,43 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdArgs p) {
   const int bg = blockIdx.y;
   const int b = bg / p.Hkv;
   const int n_last = p.qtile[((size_t)b * p.QT + p.QT - 1) * kQF + 1];
-  const int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  if (ai >= n_last) return;
   const int c4 = (threadIdx.x % TPR) * 4;
   const size_t cstride = (size_t)p.B * p.Hkv * p.S * D;
-  const size_t off = ((size_t)bg * p.S + ai) * D + c4;
-  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c <= p.nchunk; ++c) {
-    sk += *(const f32x4*)(p.dKa + c * cstride + off);
-    sv += *(const f32x4*)(p.dVa + c * cstride + off);
-  }
-  const int krow = p.anchor_pos[(size_t)b * p.S + ai];
-  const size_t o = ((size_t)bg * p.S + krow) * D + c4;
-  if constexpr (sizeof(T) == 2) {
-    *(u32x2*)((uint16_t*)p.dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
-    *(u32x2*)((uint16_t*)p.dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
-  } else {
-    *(f32x4*)((float*)p.dk + o) = sk;
-    *(f32x4*)((float*)p.dv + o) = sv;
+  // the anchor count is known on the device only: a fixed number of
+  // workgroups per (sequence, kv head) strides over it
+  for (int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR; ai < n_last; ai += gridDim.x * (256 / TPR)) {
+    const size_t off = ((size_t)bg * p.S + ai) * D + c4;
+    const int krow = p.anchor_pos[(size_t)b * p.S + ai];
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    // the partials of 4 slots in flight at once (slots past nchunk re-read
+    // the last one and are not added)
+    for (int c0 = 0; c0 <= p.nchunk; c0 += 4) {
+      f32x4 k4[4], v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t cc = (size_t)min(c0 + j, p.nchunk);
+        k4[j] = *(const f32x4*)(p.dKa + cc * cstride + off);
+        v4[j] = *(const f32x4*)(p.dVa + cc * cstride + off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool use = c0 + j <= p.nchunk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk[e] += use ? k4[j][e] : 0.f;
+          sv[e] += use ? v4[j][e] : 0.f;
+        }
+      }
+    }
+    const size_t o = ((size_t)bg * p.S + krow) * D + c4;
+    if constexpr (sizeof(T) == 2) {
+      *(u32x2*)((uint16_t*)p.dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+      *(u32x2*)((uint16_t*)p.dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+    } else {
+      *(f32x4*)((float*)p.dk + o) = sk;
+      *(f32x4*)((float*)p.dv + o) = sv;
+    }
   }
 }
 
@@ -784,7 +827,7 @@ template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   constexpr int TPR = D / Traits<T>::VEC;
   const size_t rows = (size_t)a.B * a.Hq * a.SB * kKTile;  // 64-padded rows
-  const int pre_blocks = (int)((rows + (256 / TPR) - 1) / (256 / TPR));
+  const int pre_blocks = (int)((rows + kPreRows - 1) / kPreRows);
   const int main_blocks = a.n_anchor_items + a.n_dq_items + a.n_band_items;
   const int fin_rows_per_block = 256 / (D / 4);
   hipError_t e;
@@ -795,9 +838,9 @@ static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
-                                                       a.B * a.Hkv),
-                     dim3(256), 0, stream, a);
+  const int fin_x = std::max(1, std::min((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
+                                         SEPATTN_FIN_BLOCKS / (a.B * a.Hkv)));
+  hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3(fin_x, a.B * a.Hkv), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;

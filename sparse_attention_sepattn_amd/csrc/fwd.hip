@@ -33,7 +33,10 @@ constexpr float kLazy = 8.f;
 #define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
 #endif
 #ifndef SEPATTN_FWD_OCC
-#define SEPATTN_FWD_OCC 4  // workgroups per CU the bf16 register budget targets
+#define SEPATTN_FWD_OCC 4  // workgroups per CU the bf16 d=64 register budget targets
+#endif
+#ifndef SEPATTN_FWD_OCC128
+#define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
 #endif
 #ifndef SEPATTN_FWD_DMA
 #define SEPATTN_FWD_DMA 1  // K/V tiles loaded straight into LDS
@@ -43,7 +46,7 @@ constexpr float kLazy = 8.f;
 #endif
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? SEPATTN_FWD_OCC : 1) fwd_kernel(FwdArgs p) {
+__global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPATTN_FWD_OCC : SEPATTN_FWD_OCC128) : 1) fwd_kernel(FwdArgs p) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kFwdThreads> Regs;

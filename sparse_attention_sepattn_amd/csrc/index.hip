@@ -13,7 +13,10 @@
 
 namespace sepattn {
 
-constexpr int kScanThreads = 1024;
+#ifndef SEPATTN_SCAN_THREADS
+#define SEPATTN_SCAN_THREADS 1024
+#endif
+constexpr int kScanThreads = SEPATTN_SCAN_THREADS;
 constexpr int kScanItems = 8;  // consecutive tokens per thread per chunk
 
 // One workgroup per sequence.  Chunks of kScanThreads * kScanItems tokens are
@@ -41,16 +44,32 @@ index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep, int
 
   for (int base = 0; base < S; base += kScanThreads * kScanItems) {
     const int j0 = base + t * kScanItems;
+    // every token load is issued before any is used (clamped rows past S are
+    // read but not counted)
+    int32_t tv[kScanItems];
+    if (interval <= 0) {
+#pragma unroll
+      for (int e = 0; e < kScanItems; ++e) tv[e] = tk[min(j0 + e, S - 1)];
+    }
+    // membership: ids outer, tokens inner, so each id is read once per chunk
+    bool hit[kScanItems];
+#pragma unroll
+    for (int e = 0; e < kScanItems; ++e) hit[e] = interval > 0 && (j0 + e) % interval == interval - 1;
+    if (interval <= 0) {
+#pragma unroll 4
+      for (int i = 0; i < sep.n; ++i) {
+        const int32_t id = sep.ids[i];
+#pragma unroll
+        for (int e = 0; e < kScanItems; ++e) hit[e] |= tv[e] == id;
+      }
+    }
     int f[kScanItems];
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < kScanItems; ++e) {
       const int j = j0 + e;
-      int s = 0;
-      if (j < S) {
-        s = interval > 0 ? (j % interval == interval - 1) : (is_separator(sep, tk[j]) ? 1 : 0);
-        fl[j] = (uint8_t)s;
-      }
+      const int s = hit[e] ? 1 : 0;
+      if (j < S) fl[j] = (uint8_t)s;
       f[e] = (j < S && j >= a) ? s : 0;  // separators counted from position a on
       cnt += f[e];
     }
@@ -95,21 +114,23 @@ index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep, int
   for (int j = n_init + total + t; j < S; j += kScanThreads) anc[j] = -1;
 }
 
-// Visible entries of the mask in row i over key columns [c0, c1] (c1 < S).
-__device__ __forceinline__ int row_count(int i, int c0, int c1, int a, int n,
-                                         const int32_t* __restrict__ pre) {
+// Visible entries of the mask in row i over key columns [c0, c1] (c1 < S),
+// split so that a caller can keep many prefix loads in flight: `cnt` gets the
+// window and initial-token part, and the separator part is
+// pre[*hi_ix] - pre[*lo_ix] (both 0 when it is empty).
+__device__ __forceinline__ void row_count_parts(int i, int c0, int c1, int a, int n, int* cnt, int* hi_ix,
+                                                int* lo_ix) {
   const int hi = c1 < i ? c1 : i;
-  if (hi < c0) return 0;
   const int w0 = (i - n + 1) > c0 ? (i - n + 1) : c0;
-  int cnt = hi >= w0 ? hi - w0 + 1 : 0;  // window part
+  int c = hi >= w0 ? hi - w0 + 1 : 0;  // window part (empty when hi < c0)
   const int e = hi < (i - n) ? hi : (i - n);  // last key outside the window
-  if (e >= c0) {
-    const int ie = e < a - 1 ? e : a - 1;
-    if (ie >= c0) cnt += ie - c0 + 1;  // initial tokens
-    const int s0 = c0 > a ? c0 : a;
-    if (e >= s0) cnt += pre[e + 1] - pre[s0];  // separators
-  }
-  return cnt;
+  const int ie = e < a - 1 ? e : a - 1;
+  c += ie >= c0 ? ie - c0 + 1 : 0;  // initial tokens
+  const int s0 = c0 > a ? c0 : a;
+  const bool seps = e >= s0;  // separators in [s0, e]
+  *cnt = c;
+  *hi_ix = seps ? e + 1 : 0;
+  *lo_ix = seps ? s0 : 0;
 }
 
 // Grid (QT, B): per query tile, its schedule fields and the class of every
@@ -148,7 +169,34 @@ index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
     const int c1 = min(c0 + kKTile - 1, S - 1);
     int total = 0;
     if (kj < KT && c0 <= q1) {
-      for (int i = q0 + sub; i <= q1; i += 8) total += row_count(i, c0, c1, a, n, pre);
+      if (c1 <= q0 - n) {
+        // left of every row's window: each row sees the same keys of the
+        // tile (its initial tokens and separators), so count one row
+        if (sub == 0) {
+          int c, hx, lx;
+          row_count_parts(q0, c0, c1, a, n, &c, &hx, &lx);
+          total = (q1 - q0 + 1) * (c + pre[hx] - pre[lx]);
+        }
+      } else {
+        // the 16 rows of this lane (rows past the tile are not counted), all
+        // of their prefix loads issued before any is used
+        constexpr int R = kQTile / 8;
+        int c[R], hx[R], lx[R], ph[R], pl[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int i = q0 + sub + 8 * r;
+          row_count_parts(min(i, q1), c0, c1, a, n, &c[r], &hx[r], &lx[r]);
+          if (i > q1) c[r] = hx[r] = lx[r] = 0;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          ph[r] = pre[hx[r]];
+          pl[r] = pre[lx[r]];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) total += c[r] + ph[r] - pl[r];
+      }
     }
     total += __shfl_xor(total, 1, 64);
     total += __shfl_xor(total, 2, 64);
