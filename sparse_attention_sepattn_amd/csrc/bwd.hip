@@ -28,6 +28,8 @@
 // dO^T and Q^T are read from the row-major LDS tiles with the transpose read.
 // Query-major (dQ): S^T = K Q^T as in the forward, dP^T = V dO^T,
 // dQ^T = K^T dS^T.
+#include <type_traits>
+
 #include "internal.hpp"
 #include "tile.hpp"
 
@@ -188,12 +190,24 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
   }
 }
 
+// Double-buffered LDS tiles as separate arrays: each step names its buffer
+// at compile time, so the compiler can tell a DMA into one buffer from the
+// reads of the other and does not wait for that DMA before the reads.
+template <typename T>
+struct SmemBufs {
+  T* a[2];      // Q tiles (dK/dV items), K tiles (dQ items)
+  T* b[2];      // dO tiles, V tiles
+  float* l[2];  // per-wave log2(e)*LSE and D copies (dK/dV items)
+};
+typedef std::integral_constant<int, 0> Buf0;
+typedef std::integral_constant<int, 1> Buf1;
+
 // ---------------------------------------------------------------------------
 // key-major dK/dV of one key unit (128 keys) against a range of query tiles
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool ANCHOR>
-__device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk, T* Qs, T* dOs,
-                                          float* ld_s) {
+__device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int unit, int chunk,
+                                          const SmemBufs<T>& sm) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kBwdThreads> Regs;
@@ -258,22 +272,22 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   };
   const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
-  auto issue = [&](int it, Regs& rq, Regs& ro, float& pl, float& pd) {
+  auto issue = [&](int it, auto B, Regs& rq, Regs& ro, float& pl, float& pd) {
+    constexpr int buf = decltype(B)::value;
     const int h = it_head(it);
     const int r0 = it_row0(it);
     const size_t bh = (size_t)b * p.Hq + h;
     int rows[Regs::NU];
     Regs::rows(rows, RowSrc{nullptr, r0, p.S}, tid);
     if constexpr (kDMA) {
-      DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, Qs + (it & 1) * G::ELEMS, tid);
-      DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, dOs + (it & 1) * G::ELEMS,
-                 tid);
+      DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, sm.a[buf], tid);
+      DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, sm.b[buf], tid);
       // this wave's own copy of the tile's 64 (log2(e)*LSE, D) pairs: lanes
       // 0..31 carry the 512-byte block, lanes 32..63 read past the buffer
       // (zeros into the unused half of the wave's 1 KB slot)
       const unsigned off = lane < 32 ? (unsigned)((r0 / kKTile) * 2 * kKTile * 4 + lane * 16) : ldbytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(p.LD + bh * p.SB * 2 * kKTile, ldbytes),
-                                               (__attribute__((address_space(3))) void*)(ld_s + ((it & 1) * 4 + w) * 256),
+                                               (__attribute__((address_space(3))) void*)(sm.l[buf] + w * 256),
                                                16, off, 0, 0, 0);
     } else {
       rq.issue((const T*)p.q + bh * p.S * D, rows, tid);
@@ -288,8 +302,13 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
 
   Regs rqA, roA, rqB, roB;
   float plA = 0.f, pdA = 0.f, plB = 0.f, pdB = 0.f;
-  if (n_it > 0) issue(0, rqA, roA, plA, pdA);
-  if (PF == 2 && n_it > 1) issue(1, rqB, roB, plB, pdB);
+  // anchor items: anchor count of each step's query tile, loaded one step
+  // ahead into the slot of the step's buffer parity
+  auto anchor_count_of = [&](int it) { return qt[(it_row0(it) / kQTile) * kQF + 1]; };
+  int nlim[2] = {0, 0};
+  if (ANCHOR && n_it > 0) nlim[0] = anchor_count_of(0);
+  if (n_it > 0) issue(0, Buf0{}, rqA, roA, plA, pdA);
+  if (PF == 2 && n_it > 1) issue(1, Buf1{}, rqB, roB, plB, pdB);
 
   // this lane's key rows (a lane without a key reads row 0: its column is
   // masked out of every tile and never stored)
@@ -310,11 +329,12 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     dv[db] = f32x16{};
   }
 
-  auto step = [&](int it, Regs& rq, Regs& ro, float& pl, float& pd) {
-    const int buf = it & 1;
-    T* Qb = Qs + buf * G::ELEMS;
-    T* dOb = dOs + buf * G::ELEMS;
-    float* lb = ld_s + (buf * 4 + (kDMA ? w : 0)) * 256;  // log2(e)*LSE of the tile's 64 rows
+  // step `it` reads buffer B = it & 1
+  auto step = [&](int it, auto B, Regs& rq, Regs& ro, float& pl, float& pd) {
+    constexpr int buf = decltype(B)::value;
+    T* Qb = sm.a[buf];
+    T* dOb = sm.b[buf];
+    float* lb = sm.l[buf] + (kDMA ? w : 0) * 256;  // log2(e)*LSE of the tile's 64 rows
     float* db_ = lb + kKTile;                                 // then D
     if constexpr (!kDMA) {
       rq.store(Qb, tid);
@@ -329,16 +349,19 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     __syncthreads();  // tile `it` visible; every wave is done with tile it-1's buffer
     const int r0 = it_row0(it);
     const int qi = r0 / kQTile;
-    if (it + PF < n_it) issue(it + PF, rq, ro, pl, pd);
+    if (it + PF < n_it) issue(it + PF, std::integral_constant<int, (buf + PF) & 1>{}, rq, ro, pl, pd);
+    // the anchor count of the next step's query tile, read now and used there
+    if constexpr (ANCHOR) nlim[1 - buf] = anchor_count_of(min(it + 1, n_it - 1));
 
     // query-row range [ql, qh] of the rows that see this lane's key
     int ql, qh;
     if constexpr (ANCHOR) {
-      const bool seen = krow >= 0 && kidx < qt[qi * kQF + 1];
+      const bool seen = krow >= 0 && kidx < nlim[buf];
       ql = seen ? 0 : 1;
       qh = seen ? p.S - 1 : 0;
     } else {
-      const bool in_band = krow >= 0 && krow >= qt[qi * kQF + 0];
+      // window start of the query tile (the index builder's lo)
+      const bool in_band = krow >= 0 && krow >= max(0, qi * kQTile - p.n + 1);
       ql = in_band ? krow : 1;
       qh = in_band ? q_hi : 0;
     }
@@ -429,13 +452,17 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     }
   };
 
-  if constexpr (PF == 2) {
-    for (int it = 0; it < n_it; it += 2) {
-      step(it, rqA, roA, plA, pdA);
-      if (it + 1 < n_it) step(it + 1, rqB, roB, plB, pdB);
+  {
+    Regs& rq1 = PF == 2 ? rqB : rqA;
+    Regs& ro1 = PF == 2 ? roB : roA;
+    float& pl1 = PF == 2 ? plB : plA;
+    float& pd1 = PF == 2 ? pdB : pdA;
+    int it = 0;
+    for (; it + 1 < n_it; it += 2) {
+      step(it, Buf0{}, rqA, roA, plA, pdA);
+      step(it + 1, Buf1{}, rq1, ro1, pl1, pd1);
     }
-  } else {
-    for (int it = 0; it < n_it; ++it) step(it, rqA, roA, plA, pdA);
+    if (it < n_it) step(it, Buf0{}, rqA, roA, plA, pdA);
   }
 
   // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i)
@@ -490,7 +517,7 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
 // query-major dQ of one query tile over the forward's schedule
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, T* Ks, T* Vs) {
+__device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, const SmemBufs<T>& sm) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
   typedef TileRegs<T, D, kBwdThreads> Regs;
@@ -545,12 +572,32 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   };
   const unsigned kv_bytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const __amdgpu_buffer_rsrc_t Krs = buffer_rsrc(Kg, kv_bytes), Vrs = buffer_rsrc(Vg, kv_bytes);
-  auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
+  // Source rows of anchor tiles come from the anchor list; with DMA their
+  // loads are issued one tile ahead (fetch), unconditionally with a clamped
+  // index, so no step waits on them before it can issue its DMA (resolve).
+  int arow[Regs::NU];
+  auto fetch = [&](int t) {
+    const RowSrc r = src_of(t);
+#pragma unroll
+    for (int u = 0; u < Regs::NU; ++u) arow[u] = anc[min(r.base + Regs::row_of(tid, u), r.limit - 1)];
+  };
+  auto resolve = [&](int t, int* rows) {
+    const RowSrc r = src_of(t);
+#pragma unroll
+    for (int u = 0; u < Regs::NU; ++u) {
+      const int x = r.base + Regs::row_of(tid, u);
+      rows[u] = x < r.limit ? (r.anchor ? arow[u] : x) : -1;
+    }
+  };
+  // tile t into buffer B (DMA), or into registers
+  auto issue = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+    constexpr int buf = decltype(B)::value;
     int rows[Regs::NU];
-    Regs::rows(rows, src_of(t), tid);
+    if (kDMA && t > 0) resolve(t, rows);
+    else Regs::rows(rows, src_of(t), tid);
     if constexpr (kDMA) {
-      DMA::issue(Krs, kv_bytes, rows, Ks + (t & 1) * G::ELEMS, tid);
-      DMA::issue(Vrs, kv_bytes, rows, Vs + (t & 1) * G::ELEMS, tid);
+      DMA::issue(Krs, kv_bytes, rows, sm.a[buf], tid);
+      DMA::issue(Vrs, kv_bytes, rows, sm.b[buf], tid);
     } else {
       rk.issue(Kg, rows, tid);
       rv.issue(Vg, rows, tid);
@@ -564,8 +611,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
 
   Regs rkA, rvA, rkB, rvB;
   int sA = 0, sB = 0;
-  issue(0, rkA, rvA, sA);
-  if (PF == 2 && n_tiles > 1) issue(1, rkB, rvB, sB);
+  issue(0, Buf0{}, rkA, rvA, sA);
+  if (PF == 2 && n_tiles > 1) issue(1, Buf1{}, rkB, rvB, sB);
+  if (kDMA) fetch(min(1, n_tiles - 1));
 
   frag qf[NQF], of[NQF];
 #pragma unroll
@@ -588,10 +636,11 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   const int wrow0 = q0 + 32 * w;
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
-  auto step = [&](int t, Regs& rk, Regs& rv, int& sflag) {
-    const int buf = t & 1;
-    T* K = Ks + buf * G::ELEMS;
-    T* V = Vs + buf * G::ELEMS;
+  // step t reads buffer B = t & 1
+  auto step = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+    constexpr int buf = decltype(B)::value;
+    T* K = sm.a[buf];
+    T* V = sm.b[buf];
     if constexpr (!kDMA) {
       rk.store(K, tid);
       rv.store(V, tid);
@@ -599,7 +648,10 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     const uint64_t sepbits = __ballot(sflag != 0);
     if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
     __syncthreads();
-    if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
+    if (t + PF < n_tiles) {
+      issue(t + PF, std::integral_constant<int, (buf + PF) & 1>{}, rk, rv, sflag);
+      if (kDMA) fetch(min(t + 2, n_tiles - 1));
+    }
 
     const bool anchor_tile = t >= n_band;
     bool full;
@@ -687,13 +739,16 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     }
   };
 
-  if constexpr (PF == 2) {
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(t, rkA, rvA, sA);
-      if (t + 1 < n_tiles) step(t + 1, rkB, rvB, sB);
+  {
+    Regs& rk1 = PF == 2 ? rkB : rkA;
+    Regs& rv1 = PF == 2 ? rvB : rvA;
+    int& s1 = PF == 2 ? sB : sA;
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, Buf0{}, rkA, rvA, sA);
+      step(t + 1, Buf1{}, rk1, rv1, s1);
     }
-  } else {
-    for (int t = 0; t < n_tiles; ++t) step(t, rkA, rvA, sA);
+    if (t < n_tiles) step(t, Buf0{}, rkA, rvA, sA);
   }
 
   if (q_ok) {
@@ -726,9 +781,13 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
 template <typename T, int D>
 __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main_kernel(BwdArgs p) {
   typedef TileGeom<T, D> G;
-  __shared__ __attribute__((aligned(16))) T smA[2 * G::ELEMS];
-  __shared__ __attribute__((aligned(16))) T smB[2 * G::ELEMS];
-  __shared__ __attribute__((aligned(16))) float smLD[2 * 4 * 256];  // [buffer][wave][LSE x 64, D x 64, spare]
+  __shared__ __attribute__((aligned(16))) T smA0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smA1[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smB0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smB1[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) float smL0[4 * 256];  // [wave][LSE x 64, D x 64, spare]
+  __shared__ __attribute__((aligned(16))) float smL1[4 * 256];
+  const SmemBufs<T> sm = {{smA0, smA1}, {smB0, smB1}, {smL0, smL1}};
 
   int x = blockIdx.x;
   const int BG = p.B * p.Hkv;
@@ -740,7 +799,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
     const int bg = r / p.nchunk;
     const int chunk = r - bg * p.nchunk;
     for (int unit = lane0; unit < p.units; unit += p.anchor_lanes) {
-      if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, smA, smB, smLD)) break;
+      if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, sm)) break;
       __syncthreads();  // the next unit refills the tile buffers
     }
     return;
@@ -750,7 +809,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
     const int BH = p.B * p.Hq;
     const int qi = p.QT - 1 - x / BH;
     const int bh = x % BH;
-    dq_item<T, D>(p, bh / p.Hq, bh % p.Hq, qi, smA, smB);
+    dq_item<T, D>(p, bh / p.Hq, bh % p.Hq, qi, sm);
     return;
   }
   // band items: the units of one (sequence, kv head) share query tiles, so
@@ -758,7 +817,7 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   const int li = xcd_local_index(blockIdx.x, p.n_anchor_items + p.n_dq_items, p.n_band_items);
   const int bg = li / p.units;
   const int unit = li - bg * p.units;
-  dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, smA, smB, smLD);
+  dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, sm);
 }
 
 // ---------------------------------------------------------------------------

@@ -8,6 +8,8 @@
 // Mask: SepLLM summary on atlas.scime.ai, "Approach".  Output O = M(A, V, M_b)
 // read as softmax renormalised over the kept keys ("How SepLLM Reorchestrates
 // the Language Model for Speed and Efficiency", "SepLLM's Architecture").
+#include <type_traits>
+
 #include "internal.hpp"
 #include "tile.hpp"
 
@@ -33,7 +35,7 @@ constexpr float kLazy = 8.f;
 #define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
 #endif
 #ifndef SEPATTN_FWD_OCC
-#define SEPATTN_FWD_OCC 4  // workgroups per CU the bf16 d=64 register budget targets
+#define SEPATTN_FWD_OCC 3  // workgroups per CU the bf16 d=64 register budget targets (4 spills)
 #endif
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
@@ -60,8 +62,23 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   constexpr int PF = kDMA ? 1 : ((sizeof(T) == 2 && D == 64) ? SEPATTN_FWD_PREFETCH : 1);  // tiles in flight
   typedef TileDMA<T, D, kFwdThreads> DMA;
 
-  __shared__ __attribute__((aligned(16))) T Ks[2][G::ELEMS];
-  __shared__ __attribute__((aligned(16))) T Vs[2][G::ELEMS];
+  // double buffers as separate arrays, and each step names its buffer at
+  // compile time: the compiler can then tell a DMA into one buffer from the
+  // reads of the other and does not wait for the DMA before those reads
+  __shared__ __attribute__((aligned(16))) T Ks0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T Ks1[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T Vs0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T Vs1[G::ELEMS];
+  auto kbuf = [&](auto B) -> T* {
+    if constexpr (decltype(B)::value == 0) return Ks0;
+    else return Ks1;
+  };
+  auto vbuf = [&](auto B) -> T* {
+    if constexpr (decltype(B)::value == 0) return Vs0;
+    else return Vs1;
+  };
+  constexpr std::integral_constant<int, 0> I0{};
+  constexpr std::integral_constant<int, 1> I1{};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,13 +132,33 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     return j < p.S ? (int)sepf[j] : 0;
   };
 
+  // Source rows of anchor tiles come from the anchor list.  Their loads are
+  // issued one tile ahead (fetch), unconditionally with a clamped index, so
+  // no step waits on them before it can issue its DMA (resolve).
+  int arow[Regs::NU];
+  auto fetch = [&](int t) {
+    const RowSrc r = src_of(t);
+#pragma unroll
+    for (int u = 0; u < Regs::NU; ++u) arow[u] = anc[min(r.base + Regs::row_of(tid, u), r.limit - 1)];
+  };
+  auto resolve = [&](int t, int* rows) {
+    const RowSrc r = src_of(t);
+#pragma unroll
+    for (int u = 0; u < Regs::NU; ++u) {
+      const int x = r.base + Regs::row_of(tid, u);
+      rows[u] = x < r.limit ? (r.anchor ? arow[u] : x) : -1;
+    }
+  };
+
   // prologue: the first PF tiles in flight
-  auto issue = [&](int t, Regs& rk, Regs& rv, int& sflag) {
+  // tile t into buffer B (DMA), or into registers
+  auto issue = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
     int rows[Regs::NU];
-    Regs::rows(rows, src_of(t), tid);
+    if (kDMA && t > 0) resolve(t, rows);
+    else Regs::rows(rows, src_of(t), tid);
     if constexpr (kDMA) {
-      DMA::issue(Krs, kv_bytes, rows, Ks[t & 1], tid);
-      DMA::issue(Vrs, kv_bytes, rows, Vs[t & 1], tid);
+      DMA::issue(Krs, kv_bytes, rows, kbuf(B), tid);
+      DMA::issue(Vrs, kv_bytes, rows, vbuf(B), tid);
     } else {
       rk.issue(Kg, rows, tid);
       rv.issue(Vg, rows, tid);
@@ -130,8 +167,9 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   };
   Regs rkA, rvA, rkB, rvB;
   int sA = 0, sB = 0;
-  issue(0, rkA, rvA, sA);
-  if (PF == 2 && n_tiles > 1) issue(1, rkB, rvB, sB);
+  issue(0, I0, rkA, rvA, sA);
+  if (PF == 2 && n_tiles > 1) issue(1, I1, rkB, rvB, sB);
+  if (kDMA) fetch(min(1, n_tiles - 1));
 
   frag qf[NQF];
 #pragma unroll
@@ -149,18 +187,23 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   const int wrow0 = q0 + 32 * w;
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
-  auto step = [&](int t, Regs& rk, Regs& rv, int& sflag) {
-    const int buf = t & 1;
+  // tile t from buffer B = t & 1
+  auto step = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+    constexpr int buf = decltype(B)::value;
+    constexpr std::integral_constant<int, 1 - buf> NB{};
     if constexpr (!kDMA) {
-      rk.store(Ks[buf], tid);
-      rv.store(Vs[buf], tid);
+      rk.store(kbuf(B), tid);
+      rv.store(vbuf(B), tid);
     }
     const uint64_t sepbits = __ballot(sflag != 0);
     if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
     __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
-    if (t + PF < n_tiles) issue(t + PF, rk, rv, sflag);
-    const T* K = Ks[buf];
-    const T* V = Vs[buf];
+    if (t + PF < n_tiles) {
+      issue(t + PF, NB, rk, rv, sflag);  // DMA (PF = 1) fills the other buffer
+      if (kDMA) fetch(min(t + 2, n_tiles - 1));
+    }
+    const T* K = kbuf(B);
+    const T* V = vbuf(B);
 
     // visibility (partial tiles only; bit r of vis: key r of the tile is visible)
     const bool anchor_tile = t >= n_band;
@@ -255,13 +298,16 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     }
   };
 
-  if constexpr (PF == 2) {
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(t, rkA, rvA, sA);
-      if (t + 1 < n_tiles) step(t + 1, rkB, rvB, sB);
+  {
+    Regs& rk1 = PF == 2 ? rkB : rkA;
+    Regs& rv1 = PF == 2 ? rvB : rvA;
+    int& s1 = PF == 2 ? sB : sA;
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, I0, rkA, rvA, sA);
+      step(t + 1, I1, rk1, rv1, s1);
     }
-  } else {
-    for (int t = 0; t < n_tiles; ++t) step(t, rkA, rvA, sA);
+    if (t < n_tiles) step(t, I0, rkA, rvA, sA);
   }
 
   // normalise and store
