@@ -86,7 +86,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* Dvec;  // [B,Hq,S]
-  float* LD;    // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then D (zero past S)
+  float* LD;    // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then -D (zero past S)
   float* dKa;   // [nchunk+1,B,Hkv,S,D] fp32 partials by slot and anchor index
   float* dVa;
   const uint8_t* is_sep;
@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
     if (valid[k]) p.Dvec[row[k]] = d;
     float* blk = p.LD + (bh * p.SB + r / kKTile) * (2 * kKTile);
     blk[r % kKTile] = lse2;
-    blk[kKTile + r % kKTile] = d;
+    blk[kKTile + r % kKTile] = -d;  // the dK/dV items start dP's accumulation from -D
   }
 }
 
@@ -335,7 +335,7 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     T* Qb = sm.a[buf];
     T* dOb = sm.b[buf];
     float* lb = sm.l[buf] + (kDMA ? w : 0) * 256;  // log2(e)*LSE of the tile's 64 rows
-    float* db_ = lb + kKTile;                                 // then D
+    float* db_ = lb + kKTile;                                 // then -D
     if constexpr (!kDMA) {
       rq.store(Qb, tid);
       ro.store(dOb, tid);
@@ -384,7 +384,13 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
         oo[c] = read_x<T, D>(dOb, mb, c, lane);
       }
       sacc = f32x16{};
-      pacc = f32x16{};
+      // dP - D: the accumulation starts from -D of each row
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 n4 = *(const f32x4*)&db_[32 * mb + 8 * i4 + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pacc[4 * i4 + e] = n4[e];
+      }
 #pragma unroll
       for (int c = 0; c < NF; ++c) {
         sacc = Tr::mfma(qq[c], kf[c], sacc);
@@ -408,14 +414,10 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
         for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 d4 = *(const f32x4*)&db_[32 * mb + 8 * i4 + 4 * hh];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(sacc[4 * i4 + e]);
-          sacc[4 * i4 + e] = pv;
-          pacc[4 * i4 + e] = pv * (pacc[4 * i4 + e] - d4[e]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(sacc[i]);
+        sacc[i] = pv;
+        pacc[i] = pv * pacc[i];  // pacc holds dP - D
       }
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) {
@@ -628,6 +630,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   }
   const float lse2 = q_ok ? p.lse[((size_t)b * p.Hq + h) * p.S + iq] * 1.4426950408889634f : 0.f;
   const float Di = q_ok ? p.Dvec[((size_t)b * p.Hq + h) * p.S + iq] : 0.f;
+  f32x16 negD;  // dP^T - D: every accumulation starts from -D of this lane's row
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negD[i] = -Di;
 
   f32x16 dq[NDB];
 #pragma unroll
@@ -681,7 +686,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
         vv[c] = read_x<T, D>(V, k2, c, lane);
       }
       sacc = f32x16{};
-      pacc = f32x16{};
+      pacc = negD;
 #pragma unroll
       for (int c = 0; c < NQF; ++c) {
         sacc = Tr::mfma(kk[c], qf[c], sacc);
@@ -698,7 +703,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
         for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pacc[i] = fast_exp2(sacc[i]) * (pacc[i] - Di);
+      for (int i = 0; i < 16; ++i) pacc[i] = fast_exp2(sacc[i]) * pacc[i];  // pacc holds dP^T - D
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) sf[sl] = acc_frag<T>(pacc, sl);
     };

@@ -225,24 +225,22 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
 
     // S^T = K Q^T for the live 32-key halves of the tile; each half's operands
     // are read into registers first so its MFMAs issue back to back
+    // (a dead half's accumulators are never read: the max, the exponentials
+    // and the second product all skip it)
     f32x16 sacc[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      f32x16 acc;
+      if (!live[k2]) continue;
+      frag kk[NQF];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = -INFINITY;
-      if (live[k2]) {
-        frag kk[NQF];
+      for (int c = 0; c < NQF; ++c) kk[c] = read_x<T, D>(K, k2, c, lane);
+      f32x16 acc = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NQF; ++c) kk[c] = read_x<T, D>(K, k2, c, lane);
-        acc = f32x16{};
+      for (int c = 0; c < NQF; ++c) acc = Tr::mfma(kk[c], qf[c], acc);
+      if (!full) {  // wave-uniform
+        const uint32_t vw = (uint32_t)(vis >> (32 * k2 + 4 * hh));
 #pragma unroll
-        for (int c = 0; c < NQF; ++c) acc = Tr::mfma(kk[c], qf[c], acc);
-        if (!full) {  // wave-uniform
-          const uint32_t vw = (uint32_t)(vis >> (32 * k2 + 4 * hh));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[i] = keep_or_neg_inf(acc[i], bit_mask(vw, acc_bit(i)));
-        }
+        for (int i = 0; i < 16; ++i) acc[i] = keep_or_neg_inf(acc[i], bit_mask(vw, acc_bit(i)));
       }
       sacc[k2] = acc;
     }
@@ -252,9 +250,11 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     // below 2^kLazy), which leaves the rescale of O out of most tiles.
     float mloc = -INFINITY;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int k2 = 0; k2 < 2; ++k2) {
+      if (!live[k2]) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[k2][i]);
+    }
     mloc = pair_max(mloc) * p.scale_log2;  // scale > 0
     const bool grow = mloc > m + kLazy;
     if (__any(grow)) {  // wave-uniform
