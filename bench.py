@@ -16,11 +16,16 @@ tiles; forward 4*d*E, backward 10*d*E, over batch x heads), divided by the
 measured step time (index build included).  The useful-entry count
 (visible mask entries) and the tile efficiency are reported beside it.
 
-roofline: the kernel with the largest average duration, its algorithmic
-FLOPs on the same schedule (2 GEMMs per kept entry for the forward; 7 for the
-backward main kernel: S, dP, dV, dK key-major and S, dP, dQ query-major) over
-its duration measured with HIP events on the launch stream during the timed
-steps, against the bf16 dense MFMA peak.
+roofline: the kernel with the largest average duration (its duration measured
+with HIP events on the launch stream during the timed steps), placed by its
+algorithmic work: FLOPs on the same schedule (forward 4*d*E; backward 10*d*E,
+the FlashAttention-2 count with one recompute of S) and bytes (every input
+tensor read once and every output written once: the forward reads Q, K, V
+and writes O and the LSE; the backward main kernel reads Q, K, V, dO, the
+LSE and D and writes dQ, dK, dV).  Whichever takes longer at the MI355X peak
+(bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) is the bound reported; the other
+view is given beside it.  The FLOPs the kernel executes (its dQ items
+recompute S and dP: 14*d*E) are reported too.
 
 decode: the streaming SepCache workload (B=64, 32 q / 8 kv heads, d=128,
 c=800 = 4 initial + 64 separator slots + a 256-token window, RoPE theta
@@ -226,10 +231,23 @@ def prefill_leg(args, torch, sa, synth):
     ms_step = total_ms / K
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
-    # GEMMs each kernel performs per kept entry: forward 2; backward main 7
-    # (dK/dV: S, dP, dV, dK; dQ: S, dP, dQ)
-    kernel_flops = {"fwd": 4 * d * E, "bwd_main": 8 * d * (Ea + Eb) + 6 * d * E}
-    achieved = kernel_flops[dominant] / (dom_ms * 1e-3) / 1e12
+    # algorithmic work of each kernel (see the module docstring) and the
+    # GEMMs it executes per kept entry (backward main: S, dP, dV, dK
+    # key-major and S, dP, dQ query-major)
+    q_bytes, kv_bytes, row_bytes = B * Hq * S * d * 2, B * Hkv * S * d * 2, B * Hq * S * 4
+    kernel_flops = {"fwd": 4 * d * E, "bwd_main": 10 * d * E}
+    kernel_bytes = {"fwd": 2 * q_bytes + 2 * kv_bytes + row_bytes,
+                    "bwd_main": 3 * q_bytes + 4 * kv_bytes + 2 * row_bytes}
+    executed_flops = {"fwd": 4 * d * E, "bwd_main": 8 * d * (Ea + Eb) + 6 * d * E}
+    t_mfma = kernel_flops[dominant] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = kernel_bytes[dominant] / (PEAK_HBM_GBS * 1e9)
+    tflops = kernel_flops[dominant] / (dom_ms * 1e-3) / 1e12
+    gbs = kernel_bytes[dominant] / (dom_ms * 1e-3) / 1e9
+    mfma_view = dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                     frac=round(tflops / PEAK_BF16_TFLOPS, 4))
+    hbm_view = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(gbs / PEAK_HBM_GBS, 4))
+    binding, other = (hbm_view, mfma_view) if t_hbm >= t_mfma else (mfma_view, hbm_view)
     kernel_symbol = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}[dominant]
     traffic = traffic_from_profiles(kernel_symbol)
     result = dict(
@@ -243,10 +261,12 @@ def prefill_leg(args, torch, sa, synth):
                     useful_gflop_fwd_bwd=round(14 * d * nnz / 1e9, 3), tile_efficiency=round(nnz / E, 4),
                     wall_ms_per_step=round(wall / K * 1e3, 4)),
         kernels_ms_untimed_pass={nm: round(x, 5) for nm, x in avg.items()},
-        roofline=dict(kernel=kernel_symbol, bound="mfma", achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS,
-                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                      traffic=traffic, algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
-                      avg_launch_ms=round(dom_ms, 5)),
+        roofline=dict(kernel=kernel_symbol, **binding, traffic=traffic,
+                      algorithmic_mb_per_launch=round(kernel_bytes[dominant] / 1e6, 3),
+                      algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
+                      executed_gflop_per_launch=round(executed_flops[dominant] / 1e9, 3),
+                      time_at_peak_us=dict(hbm=round(t_hbm * 1e6, 2), mfma=round(t_mfma * 1e6, 2)),
+                      other_view=other, avg_launch_ms=round(dom_ms, 5)),
     )
     result["dense_layer"] = dense_layer(args, torch, sa, (q, k, v, do), tok, sep, scale, cfg, ev_cls=Events)
     return result, inp, E_seqs
