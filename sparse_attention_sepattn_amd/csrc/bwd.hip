@@ -58,6 +58,17 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_DKDV_DMA
 #define SEPATTN_DKDV_DMA 1  // dK/dV items: Q/dO tiles and LSE/D loaded straight into LDS
 #endif
+// Anchor work items aimed at, by head size: more items spread the anchor
+// columns wider but write more fp32 partial slots.  Chosen by measurement on
+// MI355X (8x12 heads of 2048 at d=64; 8 kv heads of 8192 and 32768 at
+// d=128, where the anchor columns carry most of the backward's work and the
+// time is not monotonic in the chunk count).
+#ifndef SEPATTN_ANCHOR_ITEMS64
+#define SEPATTN_ANCHOR_ITEMS64 256
+#endif
+#ifndef SEPATTN_ANCHOR_ITEMS128
+#define SEPATTN_ANCHOR_ITEMS128 768
+#endif
 #ifndef SEPATTN_FIN_BLOCKS
 #define SEPATTN_FIN_BLOCKS 1024  // finalize workgroups in all (before the per-(b, kv head) floor of one)
 #endif
@@ -105,11 +116,13 @@ struct BwdArgs {
 };
 
 // Split of the query tiles among anchor work items, from the shapes alone:
-// aim at about 1024 (anchor tile, chunk, sequence, kv head) items, guessing
-// the anchor count from a separator density of 1/8; at most 16 chunks.
-static void anchor_split(int B, int Hkv, int S, int QT, int* nchunk, int* chunk_tiles) {
+// aim at a number of (anchor tile, chunk, sequence, kv head) items that
+// depends on the head size, guessing the anchor count from a separator
+// density of 1/8; at most 16 chunks.
+static void anchor_split(int B, int Hkv, int S, int QT, int d, int* nchunk, int* chunk_tiles) {
   const long units_guess = (4 + S / 8 + 127) / 128 + 1;
-  long n = (1024 + (long)B * Hkv * units_guess - 1) / ((long)B * Hkv * units_guess);
+  const long target = d <= 64 ? SEPATTN_ANCHOR_ITEMS64 : SEPATTN_ANCHOR_ITEMS128;
+  long n = (target + (long)B * Hkv * units_guess - 1) / ((long)B * Hkv * units_guess);
   if (n < 1) n = 1;
   if (n > 16) n = 16;
   if (n > QT) n = QT;
@@ -881,7 +894,7 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   const int QT = (S + kQTile - 1) / kQTile;
   int nchunk, ct;
-  anchor_split(B, Hkv, S, QT, &nchunk, &ct);
+  anchor_split(B, Hkv, S, QT, d, &nchunk, &ct);
   const size_t SB = (S + kKTile - 1) / kKTile;
   return a256((size_t)B * Hq * S * 4) + a256((size_t)B * Hq * SB * 2 * kKTile * 4) +
          2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
@@ -930,7 +943,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.LD = (float*)w;
   w += a256((size_t)sh.B * sh.Hq * a.SB * 2 * kKTile * 4);
   a.QT = (sh.S + kQTile - 1) / kQTile;
-  anchor_split(sh.B, sh.Hkv, sh.S, a.QT, &a.nchunk, &a.chunk_tiles);
+  anchor_split(sh.B, sh.Hkv, sh.S, a.QT, sh.d, &a.nchunk, &a.chunk_tiles);
   a.dKa = (float*)w;
   w += a256((size_t)(a.nchunk + 1) * sh.B * sh.Hkv * sh.S * sh.d * 4);
   a.dVa = (float*)w;
