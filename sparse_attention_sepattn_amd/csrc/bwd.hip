@@ -39,9 +39,9 @@ constexpr int kBwdThreads = 256;
 constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
 constexpr int kPreRows = 128;    // rows of D per workgroup of the pre kernel
 
-// Workgroups per CU the register budget targets, and how many tiles ahead
-// global loads are issued: the d=128 and fp32 kernels keep more operands
-// resident than fit two waves per SIMD with two tiles in flight.
+// Workgroups per CU the register budget of the main kernel targets: the
+// d=128 and fp32 kernels keep more operands resident (key fragments and
+// dK/dV accumulators) than fit two waves per SIMD.
 #ifndef SEPATTN_BWD_OCC
 #define SEPATTN_BWD_OCC 2
 #endif
@@ -52,12 +52,6 @@ template <typename T, int D>
 constexpr int bwd_occupancy() {
   return sizeof(T) == 2 ? (D == 64 ? SEPATTN_BWD_OCC : SEPATTN_BWD_OCC128) : 1;
 }
-#ifndef SEPATTN_DKDV_PREFETCH
-#define SEPATTN_DKDV_PREFETCH 1
-#endif
-#ifndef SEPATTN_DKDV_DMA
-#define SEPATTN_DKDV_DMA 1  // dK/dV items: Q/dO tiles and LSE/D loaded straight into LDS
-#endif
 // Anchor work items aimed at, by head size: more items spread the anchor
 // columns wider but write more fp32 partial slots.  Chosen by measurement on
 // MI355X (8x12 heads of 2048 at d=64; 8 kv heads of 8192 and 32768 at
@@ -72,19 +66,9 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_FIN_BLOCKS
 #define SEPATTN_FIN_BLOCKS 1024  // finalize workgroups in all (before the per-(b, kv head) floor of one)
 #endif
-#ifndef SEPATTN_DQ_DMA
-#define SEPATTN_DQ_DMA 1  // dQ: K/V tiles loaded straight into LDS
-#endif
 #ifndef SEPATTN_DQ_INTERLEAVE
 #define SEPATTN_DQ_INTERLEAVE 1  // interleaved order when both 32-key halves of a tile are live
 #endif
-#ifndef SEPATTN_DQ_PREFETCH
-#define SEPATTN_DQ_PREFETCH 1
-#endif
-template <typename T, int D, bool KEY_MAJOR>
-constexpr int bwd_prefetch() {
-  return (sizeof(T) == 2 && D == 64) ? (KEY_MAJOR ? SEPATTN_DKDV_PREFETCH : SEPATTN_DQ_PREFETCH) : 1;
-}
 
 struct BwdArgs {
   const void* q;
@@ -223,15 +207,13 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
                                           const SmemBufs<T>& sm) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
-  typedef TileRegs<T, D, kBwdThreads> Regs;
+  typedef TileRows<T, D, kBwdThreads> Regs;
   typedef typename Tr::frag frag;
   constexpr int EPL = Tr::EPL;
   constexpr int KSTEP = Tr::KSTEP;
   constexpr int NF = D / KSTEP;    // K/V fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of dK^T / dV^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps over one 32-query block
-  constexpr bool kDMA = SEPATTN_DKDV_DMA;  // Q/dO tiles and LSE/D go global -> LDS directly
-  constexpr int PF = kDMA ? 1 : bwd_prefetch<T, D, true>();
   typedef TileDMA<T, D, kBwdThreads> DMA;
 
   const int tid = threadIdx.x;
@@ -285,43 +267,31 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   };
   const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
-  auto issue = [&](int it, auto B, Regs& rq, Regs& ro, float& pl, float& pd) {
+  // Q and dO tiles of step `it` straight into LDS buffer B
+  auto issue = [&](int it, auto B) {
     constexpr int buf = decltype(B)::value;
     const int h = it_head(it);
     const int r0 = it_row0(it);
     const size_t bh = (size_t)b * p.Hq + h;
     int rows[Regs::NU];
     Regs::rows(rows, RowSrc{nullptr, r0, p.S}, tid);
-    if constexpr (kDMA) {
-      DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, sm.a[buf], tid);
-      DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, sm.b[buf], tid);
-      // this wave's own copy of the tile's 64 (log2(e)*LSE, D) pairs: lanes
-      // 0..31 carry the 512-byte block, lanes 32..63 read past the buffer
-      // (zeros into the unused half of the wave's 1 KB slot)
-      const unsigned off = lane < 32 ? (unsigned)((r0 / kKTile) * 2 * kKTile * 4 + lane * 16) : ldbytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(p.LD + bh * p.SB * 2 * kKTile, ldbytes),
-                                               (__attribute__((address_space(3))) void*)(sm.l[buf] + w * 256),
-                                               16, off, 0, 0, 0);
-    } else {
-      rq.issue((const T*)p.q + bh * p.S * D, rows, tid);
-      ro.issue((const T*)p.dout + bh * p.S * D, rows, tid);
-      if (tid < kKTile) {
-        const float* blk = p.LD + (bh * p.SB + r0 / kKTile) * 2 * kKTile;
-        pl = blk[tid];
-        pd = blk[kKTile + tid];
-      }
-    }
+    DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, sm.a[buf], tid);
+    DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, sm.b[buf], tid);
+    // this wave's own copy of the tile's 64 (log2(e)*LSE, -D) pairs: lanes
+    // 0..31 carry the 512-byte block, lanes 32..63 read past the buffer
+    // (zeros into the unused half of the wave's 1 KB slot)
+    const unsigned off = lane < 32 ? (unsigned)((r0 / kKTile) * 2 * kKTile * 4 + lane * 16) : ldbytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(p.LD + bh * p.SB * 2 * kKTile, ldbytes),
+                                             (__attribute__((address_space(3))) void*)(sm.l[buf] + w * 256),
+                                             16, off, 0, 0, 0);
   };
 
-  Regs rqA, roA, rqB, roB;
-  float plA = 0.f, pdA = 0.f, plB = 0.f, pdB = 0.f;
   // anchor items: anchor count of each step's query tile, loaded one step
   // ahead into the slot of the step's buffer parity
   auto anchor_count_of = [&](int it) { return qt[(it_row0(it) / kQTile) * kQF + 1]; };
   int nlim[2] = {0, 0};
   if (ANCHOR && n_it > 0) nlim[0] = anchor_count_of(0);
-  if (n_it > 0) issue(0, Buf0{}, rqA, roA, plA, pdA);
-  if (PF == 2 && n_it > 1) issue(1, Buf1{}, rqB, roB, plB, pdB);
+  if (n_it > 0) issue(0, Buf0{});
 
   // this lane's key rows (a lane without a key reads row 0: its column is
   // masked out of every tile and never stored)
@@ -343,26 +313,17 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   }
 
   // step `it` reads buffer B = it & 1
-  auto step = [&](int it, auto B, Regs& rq, Regs& ro, float& pl, float& pd) {
+  auto step = [&](int it, auto B) {
     constexpr int buf = decltype(B)::value;
     T* Qb = sm.a[buf];
     T* dOb = sm.b[buf];
-    float* lb = sm.l[buf] + (kDMA ? w : 0) * 256;  // log2(e)*LSE of the tile's 64 rows
-    float* db_ = lb + kKTile;                                 // then -D
-    if constexpr (!kDMA) {
-      rq.store(Qb, tid);
-      ro.store(dOb, tid);
-      if (tid < kKTile) {
-        lb[tid] = pl;
-        db_[tid] = pd;
-      }
-    } else {
-      wait_vm_all();  // this wave's part of tile `it` (and its LSE/D copy) has landed in LDS
-    }
+    float* lb = sm.l[buf] + w * 256;  // log2(e)*LSE of the tile's 64 rows
+    float* db_ = lb + kKTile;         // then -D
+    wait_vm_all();    // this wave's part of tile `it` (and its LSE/D copy) has landed in LDS
     __syncthreads();  // tile `it` visible; every wave is done with tile it-1's buffer
     const int r0 = it_row0(it);
     const int qi = r0 / kQTile;
-    if (it + PF < n_it) issue(it + PF, std::integral_constant<int, (buf + PF) & 1>{}, rq, ro, pl, pd);
+    if (it + 1 < n_it) issue(it + 1, std::integral_constant<int, 1 - buf>{});
     // the anchor count of the next step's query tile, read now and used there
     if constexpr (ANCHOR) nlim[1 - buf] = anchor_count_of(min(it + 1, n_it - 1));
 
@@ -468,16 +429,12 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   };
 
   {
-    Regs& rq1 = PF == 2 ? rqB : rqA;
-    Regs& ro1 = PF == 2 ? roB : roA;
-    float& pl1 = PF == 2 ? plB : plA;
-    float& pd1 = PF == 2 ? pdB : pdA;
     int it = 0;
     for (; it + 1 < n_it; it += 2) {
-      step(it, Buf0{}, rqA, roA, plA, pdA);
-      step(it + 1, Buf1{}, rq1, ro1, pl1, pd1);
+      step(it, Buf0{});
+      step(it + 1, Buf1{});
     }
-    if (it < n_it) step(it, Buf0{}, rqA, roA, plA, pdA);
+    if (it < n_it) step(it, Buf0{});
   }
 
   // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i)
@@ -535,15 +492,13 @@ template <typename T, int D>
 __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, const SmemBufs<T>& sm) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
-  typedef TileRegs<T, D, kBwdThreads> Regs;
+  typedef TileRows<T, D, kBwdThreads> Regs;
   typedef typename Tr::frag frag;
   constexpr int EPL = Tr::EPL;
   constexpr int KSTEP = Tr::KSTEP;
   constexpr int NQF = D / KSTEP;
   constexpr int NDB = D / 32;
   constexpr int SPB = 32 / KSTEP;
-  constexpr bool kDMA = SEPATTN_DQ_DMA;  // K/V tiles go global -> LDS directly
-  constexpr int PF = kDMA ? 1 : bwd_prefetch<T, D, false>();
   typedef TileDMA<T, D, kBwdThreads> DMA;
 
   const int tid = threadIdx.x;
@@ -587,9 +542,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   };
   const unsigned kv_bytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const __amdgpu_buffer_rsrc_t Krs = buffer_rsrc(Kg, kv_bytes), Vrs = buffer_rsrc(Vg, kv_bytes);
-  // Source rows of anchor tiles come from the anchor list; with DMA their
-  // loads are issued one tile ahead (fetch), unconditionally with a clamped
-  // index, so no step waits on them before it can issue its DMA (resolve).
+  // Source rows of anchor tiles come from the anchor list; their loads are
+  // issued one tile ahead (fetch), unconditionally with a clamped index, so
+  // no step waits on them before it can issue its DMA (resolve).
   int arow[Regs::NU];
   auto fetch = [&](int t) {
     const RowSrc r = src_of(t);
@@ -604,19 +559,16 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
       rows[u] = x < r.limit ? (r.anchor ? arow[u] : x) : -1;
     }
   };
-  // tile t into buffer B (DMA), or into registers
-  auto issue = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+  // K and V tiles of tile t straight into LDS buffer B (its separator
+  // flags, for band tiles, into sflag)
+  int sflag = 0;
+  auto issue = [&](int t, auto B) {
     constexpr int buf = decltype(B)::value;
     int rows[Regs::NU];
-    if (kDMA && t > 0) resolve(t, rows);
+    if (t > 0) resolve(t, rows);
     else Regs::rows(rows, src_of(t), tid);
-    if constexpr (kDMA) {
-      DMA::issue(Krs, kv_bytes, rows, sm.a[buf], tid);
-      DMA::issue(Vrs, kv_bytes, rows, sm.b[buf], tid);
-    } else {
-      rk.issue(Kg, rows, tid);
-      rv.issue(Vg, rows, tid);
-    }
+    DMA::issue(Krs, kv_bytes, rows, sm.a[buf], tid);
+    DMA::issue(Vrs, kv_bytes, rows, sm.b[buf], tid);
     sflag = 0;
     if (t < n_band) {
       const int j = (kb + t) * kKTile + lane;
@@ -624,11 +576,8 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     }
   };
 
-  Regs rkA, rvA, rkB, rvB;
-  int sA = 0, sB = 0;
-  issue(0, Buf0{}, rkA, rvA, sA);
-  if (PF == 2 && n_tiles > 1) issue(1, Buf1{}, rkB, rvB, sB);
-  if (kDMA) fetch(min(1, n_tiles - 1));
+  issue(0, Buf0{});
+  fetch(min(1, n_tiles - 1));
 
   frag qf[NQF], of[NQF];
 #pragma unroll
@@ -655,20 +604,16 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
   // step t reads buffer B = t & 1
-  auto step = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+  auto step = [&](int t, auto B) {
     constexpr int buf = decltype(B)::value;
     T* K = sm.a[buf];
     T* V = sm.b[buf];
-    if constexpr (!kDMA) {
-      rk.store(K, tid);
-      rv.store(V, tid);
-    }
     const uint64_t sepbits = __ballot(sflag != 0);
-    if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
+    wait_vm_all();  // this wave's part of tile t has landed in LDS
     __syncthreads();
-    if (t + PF < n_tiles) {
-      issue(t + PF, std::integral_constant<int, (buf + PF) & 1>{}, rk, rv, sflag);
-      if (kDMA) fetch(min(t + 2, n_tiles - 1));
+    if (t + 1 < n_tiles) {
+      issue(t + 1, std::integral_constant<int, 1 - buf>{});
+      fetch(min(t + 2, n_tiles - 1));
     }
 
     const bool anchor_tile = t >= n_band;
@@ -758,15 +703,12 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
   };
 
   {
-    Regs& rk1 = PF == 2 ? rkB : rkA;
-    Regs& rv1 = PF == 2 ? rvB : rvA;
-    int& s1 = PF == 2 ? sB : sA;
     int t = 0;
     for (; t + 1 < n_tiles; t += 2) {
-      step(t, Buf0{}, rkA, rvA, sA);
-      step(t + 1, Buf1{}, rk1, rv1, s1);
+      step(t, Buf0{});
+      step(t + 1, Buf1{});
     }
-    if (t < n_tiles) step(t, Buf0{}, rkA, rvA, sA);
+    if (t < n_tiles) step(t, Buf0{});
   }
 
   if (q_ok) {

@@ -40,26 +40,18 @@ constexpr float kLazy = 8.f;
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
 #endif
-#ifndef SEPATTN_FWD_DMA
-#define SEPATTN_FWD_DMA 1  // K/V tiles loaded straight into LDS
-#endif
-#ifndef SEPATTN_FWD_PREFETCH
-#define SEPATTN_FWD_PREFETCH 1
-#endif
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPATTN_FWD_OCC : SEPATTN_FWD_OCC128) : 1) fwd_kernel(FwdArgs p) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
-  typedef TileRegs<T, D, kFwdThreads> Regs;
+  typedef TileRows<T, D, kFwdThreads> Regs;
   typedef typename Tr::frag frag;
   constexpr int EPL = Tr::EPL;
   constexpr int KSTEP = Tr::KSTEP;
   constexpr int NQF = D / KSTEP;   // Q fragments per lane
   constexpr int NDB = D / 32;      // 32-row blocks of O^T
   constexpr int SPB = 32 / KSTEP;  // MFMA steps per 32-key block
-  constexpr bool kDMA = SEPATTN_FWD_DMA;  // tiles go global -> LDS directly
-  constexpr int PF = kDMA ? 1 : ((sizeof(T) == 2 && D == 64) ? SEPATTN_FWD_PREFETCH : 1);  // tiles in flight
   typedef TileDMA<T, D, kFwdThreads> DMA;
 
   // double buffers as separate arrays, and each step names its buffer at
@@ -150,26 +142,20 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     }
   };
 
-  // prologue: the first PF tiles in flight
-  // tile t into buffer B (DMA), or into registers
-  auto issue = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+  // tile t straight into LDS buffer B (its separator flags, for band tiles,
+  // into sflag)
+  int sflag = 0;
+  auto issue = [&](int t, auto B) {
     int rows[Regs::NU];
-    if (kDMA && t > 0) resolve(t, rows);
+    if (t > 0) resolve(t, rows);
     else Regs::rows(rows, src_of(t), tid);
-    if constexpr (kDMA) {
-      DMA::issue(Krs, kv_bytes, rows, kbuf(B), tid);
-      DMA::issue(Vrs, kv_bytes, rows, vbuf(B), tid);
-    } else {
-      rk.issue(Kg, rows, tid);
-      rv.issue(Vg, rows, tid);
-    }
+    DMA::issue(Krs, kv_bytes, rows, kbuf(B), tid);
+    DMA::issue(Vrs, kv_bytes, rows, vbuf(B), tid);
     sflag = sep_flag(t);
   };
-  Regs rkA, rvA, rkB, rvB;
-  int sA = 0, sB = 0;
-  issue(0, I0, rkA, rvA, sA);
-  if (PF == 2 && n_tiles > 1) issue(1, I1, rkB, rvB, sB);
-  if (kDMA) fetch(min(1, n_tiles - 1));
+  // prologue: tile 0 in flight, the anchor rows of tile 1 requested
+  issue(0, I0);
+  fetch(min(1, n_tiles - 1));
 
   frag qf[NQF];
 #pragma unroll
@@ -188,19 +174,15 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   const int wrow1 = min(wrow0 + 31, p.S - 1);
 
   // tile t from buffer B = t & 1
-  auto step = [&](int t, auto B, Regs& rk, Regs& rv, int& sflag) {
+  auto step = [&](int t, auto B) {
     constexpr int buf = decltype(B)::value;
     constexpr std::integral_constant<int, 1 - buf> NB{};
-    if constexpr (!kDMA) {
-      rk.store(kbuf(B), tid);
-      rv.store(vbuf(B), tid);
-    }
     const uint64_t sepbits = __ballot(sflag != 0);
-    if constexpr (kDMA) wait_vm_all();  // this wave's part of tile t has landed in LDS
+    wait_vm_all();    // this wave's part of tile t has landed in LDS
     __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
-    if (t + PF < n_tiles) {
-      issue(t + PF, NB, rk, rv, sflag);  // DMA (PF = 1) fills the other buffer
-      if (kDMA) fetch(min(t + 2, n_tiles - 1));
+    if (t + 1 < n_tiles) {
+      issue(t + 1, NB);  // the next tile fills the other buffer
+      fetch(min(t + 2, n_tiles - 1));
     }
     const T* K = kbuf(B);
     const T* V = vbuf(B);
@@ -299,15 +281,12 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   };
 
   {
-    Regs& rk1 = PF == 2 ? rkB : rkA;
-    Regs& rv1 = PF == 2 ? rvB : rvA;
-    int& s1 = PF == 2 ? sB : sA;
     int t = 0;
     for (; t + 1 < n_tiles; t += 2) {
-      step(t, I0, rkA, rvA, sA);
-      step(t + 1, I1, rk1, rv1, s1);
+      step(t, I0);
+      step(t + 1, I1);
     }
-    if (t < n_tiles) step(t, I0, rkA, rvA, sA);
+    if (t < n_tiles) step(t, I0);
   }
 
   // normalise and store

@@ -98,15 +98,14 @@ struct RowSrc {
   }
 };
 
-// One 64-row tile of a [rows, D] tensor, global -> registers -> LDS.  Thread
-// tid owns NU 16-byte chunks: unit u is row tid/CH + (NT/CH)*u, chunk tid%CH,
-// so consecutive lanes read consecutive chunks of a row.
+// The rows of one 64-row tile of a [rows, D] tensor that thread tid fetches:
+// NU 16-byte chunks, unit u in row tid/CH + (NT/CH)*u, chunk tid%CH, so
+// consecutive lanes take consecutive chunks of a row.
 template <typename T, int D, int NT>
-struct TileRegs {
+struct TileRows {
   typedef TileGeom<T, D> G;
   static constexpr int NU = kKTile * G::CH / NT;
   static_assert(NU * NT == kKTile * G::CH, "tile must split evenly over the workgroup");
-  u32x4 r[NU];
 
   static __device__ __forceinline__ int row_of(int tid, int u) { return tid / G::CH + (NT / G::CH) * u; }
 
@@ -115,26 +114,12 @@ struct TileRegs {
 #pragma unroll
     for (int u = 0; u < NU; ++u) out[u] = src.row(row_of(tid, u));
   }
-  __device__ __forceinline__ void issue(const T* __restrict__ g, const int* srow, int tid) {
-    const int cc = tid % G::CH;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (srow[u] >= 0) v = *(const u32x4*)(g + (size_t)srow[u] * D + cc * Traits<T>::VEC);
-      r[u] = v;
-    }
-  }
-  __device__ __forceinline__ void store(T* __restrict__ s, int tid) const {
-    const int cc = tid % G::CH;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) *(u32x4*)(s + G::at(row_of(tid, u), cc * Traits<T>::VEC)) = r[u];
-  }
 };
 
-// The same 64-row tile loaded straight from global memory into LDS
+// A 64-row tile loaded straight from global memory into LDS
 // (buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at
 // M0 + 16*l), so no registers hold the tile in flight.  A wave's instruction
-// u fills 1 KB of LDS, the rows TileRegs::row_of gives its lanes; each lane
+// u fills 1 KB of LDS, the rows TileRows::row_of gives its lanes; each lane
 // fetches the global chunk that the swizzle puts at its LDS position.  Rows
 // with srow < 0 use an offset past the buffer's size, which the hardware
 // range check turns into zeros.  Completion is counted by vmcnt: the caller
@@ -142,7 +127,7 @@ struct TileRegs {
 template <typename T, int D, int NT>
 struct TileDMA {
   typedef TileGeom<T, D> G;
-  typedef TileRegs<T, D, NT> R;
+  typedef TileRows<T, D, NT> R;
   static constexpr int NU = R::NU;
   static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned src_bytes, const int* srow,
                                                T* tile, int tid) {
