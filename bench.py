@@ -27,6 +27,11 @@ LSE and D and writes dQ, dK, dV).  Whichever takes longer at the MI355X peak
 view is given beside it.  The FLOPs the kernel executes (its dQ items
 recompute S and dP: 14*d*E) are reported too.
 
+other_configs: the d=128 shapes (Llama-3-8B-shaped prefill, B1 32/8 heads,
+8192 tokens, n=256; 32768 tokens with bursty separators), whole steps and
+the forward alone, kept-tile TFLOP/s on the same counting; reported beside
+the main workload, not part of its value (--no-long skips them).
+
 decode: the streaming SepCache workload (B=64, 32 q / 8 kv heads, d=128,
 c=800 = 4 initial + 64 separator slots + a 256-token window, RoPE theta
 500000 by slot), 4096 steps of update + decode; HBM GB/s of the decode kernel
@@ -312,6 +317,71 @@ def dense_layer(args, torch, sa, tensors, tok, sep, scale, cfg, ev_cls):
                 causal_TFLOPs=round(14 * d * causal / (ms * 1e-3) / 1e12, 3))
 
 
+def long_configs(args, torch, sa, synth):
+    """The d=128 prefill/training shapes (Llama-3-8B-shaped prefill at 8192
+    tokens, and 32768 tokens with bursty separators): whole steps (index,
+    forward, backward) timed with events, then the forward alone.  Reported
+    beside the main workload, not part of its value."""
+    out = {}
+    for name, steps in (("llama3_8b_prefill", 10), ("long_context_32k", 4)):
+        cfg = synth.CONFIGS[name]
+        B, Hq, Hkv, S, d, a, n = (cfg[x] for x in ("B", "Hq", "Hkv", "S", "d", "a", "n"))
+        inp = synth.prefill_inputs(cfg, with_grad=True)
+        dev = torch.device("cuda:0")
+
+        def bf(x):
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        q, k, v, do = bf(inp["q"]), bf(inp["k"]), bf(inp["v"]), bf(inp["do"])
+        tok = torch.from_numpy(inp["tok"]).to(dev)
+        sep, scale = inp["sep"], float(inp["scale"])
+        del inp
+        idx = sa.Index(B, S, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(sa.bwd_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8, device=dev)
+        ev = Events()
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step(fe=None):
+            sa.build_index(tok, sep, a, n, index=idx)
+            if fe is not None:
+                ev.record(fe[0], stream)
+            sa.fwd(q, k, v, idx, scale, o=o, lse=lse)
+            if fe is not None:
+                ev.record(fe[1], stream)
+            sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+
+        for _ in range(3):
+            step()
+        t0, t1 = ev.new(2)
+        torch.cuda.synchronize()
+        ev.record(t0, stream)
+        for _ in range(steps):
+            step()
+        ev.record(t1, stream)
+        torch.cuda.synchronize()
+        ms_step = ev.ms(t0, t1) / steps
+        fmarks = [ev.new(2) for _ in range(steps)]
+        for fe in fmarks:
+            step(fe)
+        torch.cuda.synchronize()
+        ms_fwd = float(np.mean([ev.ms(fe[0], fe[1]) for fe in fmarks]))
+        ev.close()
+        qtile = idx.qtile.cpu().numpy()
+        pref = idx.sep_prefix.cpu().numpy()
+        E = sum(schedule_counts(qtile[b], pref[b], a, n, S)[0] for b in range(B)) * Hq
+        fwd_tf = 4 * d * E / (ms_fwd * 1e-3) / 1e12
+        out[name] = dict(B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, a=a, n=n, bursty=bool(cfg.get("bursty")),
+                         steps=steps, ms_per_step=round(ms_step, 4), fwd_ms=round(ms_fwd, 4),
+                         kept_tile_TFLOPs_fwd_bwd=round(14 * d * E / (ms_step * 1e-3) / 1e12, 3),
+                         fwd_TFLOPs=round(fwd_tf, 3), fwd_frac_of_mfma_peak=round(fwd_tf / PEAK_BF16_TFLOPS, 4))
+        del q, k, v, do, o, lse, dq, dk, dv, ws, idx, tok
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_leg(args, torch, sa, synth):
     cfg = synth.CONFIGS["sepcache_decode"]
     B, Hq, Hkv, d, c, a, s, w = (cfg[x] for x in ("B", "Hq", "Hkv", "d", "c", "a", "s", "w"))
@@ -497,6 +567,7 @@ def main():
     ap.add_argument("--decode-breakdown-steps", type=int, default=1024,
                     help="steps of the untimed per-kernel breakdown pass of the decode leg (0: none)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the d=128 Llama-shaped and 32k-token steps")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -526,6 +597,11 @@ def main():
     log("prefill/training leg ...")
     result, inp, E_seqs = prefill_leg(args, torch, sa, synth)
     log(f"  {result['value']} TFLOP/s, {result['ms_per_step']} ms/step")
+    if not args.no_long:
+        log("d=128 prefill/training shapes ...")
+        result["other_configs"] = long_configs(args, torch, sa, synth)
+        for nm, r in result["other_configs"].items():
+            log(f"  {nm}: {r['ms_per_step']} ms/step, forward {r['fwd_ms']} ms = {r['fwd_TFLOPs']} TFLOP/s")
     if not args.no_decode:
         log("decode leg ...")
         result["decode"] = decode_leg(args, torch, sa, synth)
