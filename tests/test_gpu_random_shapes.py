@@ -1,0 +1,90 @@
+"""Randomised GPU parity sweep over seeded shapes: lengths on and off the tile
+sizes, GQA ratios 1/2/4, both head sizes and dtypes, initial-token counts
+0..8, windows from 1 to beyond S, separator densities from none to all.  For
+every case the index is bit-exact against the oracle's direct counting and
+forward and backward are held to the tolerances of the dedicated tests (the
+forward and backward modules state their derivation):
+  * O: max-abs 1e-4 (fp32) / 2e-2 (bf16); LSE: 1e-4 / 2e-3;
+  * dQ, dK, dV: max-rel 1e-4 (fp32) / 3e-2 (bf16), Frobenius-rel 1e-2 (bf16);
+    a gradient that is zero by construction to an absolute 1e-5 / 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention, sepmask
+from tests.gpu_util import dev_tensor, host_f64, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(count=40, seed=20261203):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        S = int(r.choice([1, 2, 63, 64, 65, 127, 129, 200, 511, 777, 1025, 1500, 2049]))
+        B = int(r.integers(1, 3))
+        Hkv = int(r.integers(1, 3))
+        grp = int(r.choice([1, 2, 4]))
+        if S > 1024:  # keep the fp64 oracle to seconds
+            B, Hkv, grp = 1, 1, min(grp, 2)
+        d = int(r.choice([64, 128]))
+        dt = "bf16" if r.random() < 0.75 else "f32"
+        a = int(r.integers(0, 9))
+        n = int(r.choice([1, 7, 64, 100, 256, 3000]))
+        p = float(r.choice([0.0, 0.03, 0.1, 0.4, 1.0]))
+        out.append((S, B, Hkv * grp, Hkv, d, dt, a, n, p, 7000 + i))
+    return out
+
+
+def _grad_check(got, ref, dt, what):
+    for name, x, y in zip(("dq", "dk", "dv"), got, ref):
+        if np.abs(y).max() <= 1e-9:
+            assert np.abs(x).max() <= (1e-5 if dt == "f32" else 1e-3), (what, name)
+            continue
+        rmax = np.abs(x - y).max() / np.abs(y).max()
+        rfro = np.linalg.norm(x - y) / np.linalg.norm(y)
+        say(f"  {what} {name}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+        if dt == "f32":
+            assert rmax <= 1e-4, (what, name, rmax)
+        else:
+            assert rmax <= 3e-2 and rfro <= 1e-2, (what, name, rmax, rfro)
+
+
+@pytest.mark.parametrize("case", _cases())
+def test_random_shape(case):
+    require_gpu()
+    import sparse_attention_sepattn_amd as sa
+    S, B, Hq, Hkv, d, dt, a, n, p, seed = case
+    say(f"random shape S={S} B={B} Hq={Hq} Hkv={Hkv} d={d} {dt} a={a} n={n} p_sep={p} seed={seed}")
+    cfg = dict(seed=seed, B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, dtype=dt, vocab=1000, p_sep=p, bursty=False,
+               a=a, n=n, bwd=True)
+    inp = synth.prefill_inputs(cfg)
+    tok, sep = inp["tok"], inp["sep"]
+
+    idx = sa.build_index(torch.from_numpy(tok).cuda(), sep, a, n)
+    q, k, v, do = (dev_tensor(inp[x], dt) for x in ("q", "k", "v", "do"))
+    o, lse = sa.fwd(q, k, v, idx, inp["scale"])
+    dq, dk, dv = sa.bwd(q, k, v, o, lse, do, idx, inp["scale"])
+    torch.cuda.synchronize()
+
+    for b in range(B):
+        ref = sepmask.build_index(tok[b], sep, a, n)
+        assert np.array_equal(idx.is_sep[b].cpu().numpy(), ref["is_sep"])
+        assert np.array_equal(idx.sep_prefix[b].cpu().numpy(), ref["sep_prefix"])
+        assert np.array_equal(idx.anchor_pos[b].cpu().numpy(), ref["anchor_pos"])
+        assert int(idx.anchor_count[b]) == ref["anchor_count"]
+        assert np.array_equal(idx.qtile[b].cpu().numpy()[:, :6], ref["qtile"])
+        assert np.array_equal(idx.tile_class[b].cpu().numpy(), ref["tile_class"])
+
+    ro, rl = attention.attention_forward(inp["qf"], inp["kf"], inp["vf"], tok, sep, a, n, scale=inp["scale"])
+    to, tl = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2e-3)}[dt]
+    eo, el = np.abs(host_f64(o) - ro).max(), np.abs(lse.cpu().numpy().astype(np.float64) - rl).max()
+    say(f"  fwd: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+    assert eo <= to and el <= tl, (eo, el)
+
+    ref_g = attention.attention_backward(inp["qf"], inp["kf"], inp["vf"], inp["dof"], tok, sep, a, n,
+                                         scale=inp["scale"])
+    _grad_check((host_f64(dq), host_f64(dk), host_f64(dv)), ref_g, dt, f"S={S}")
