@@ -63,6 +63,22 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_ANCHOR_ITEMS128
 #define SEPATTN_ANCHOR_ITEMS128 768
 #endif
+// bf16 dQ items in a kernel of their own after the main one, at SPLIT_OCC
+// waves per SIMD.  Measured on MI355X: 6% off the main backward at d=128
+// (8 kv heads of 32768); slower at d=64 (8x12 heads of 2048), where the dQ
+// items already share the main kernel's two waves per SIMD at no register cost.
+#ifndef SEPATTN_DQ_SPLIT
+#define SEPATTN_DQ_SPLIT 1
+#endif
+#ifndef SEPATTN_DQ_SPLIT_OCC
+#define SEPATTN_DQ_SPLIT_OCC 2
+#endif
+#ifndef SEPATTN_DQ_SPLIT64
+#define SEPATTN_DQ_SPLIT64 0
+#endif
+#ifndef SEPATTN_DQ_SPLIT_OCC64
+#define SEPATTN_DQ_SPLIT_OCC64 3
+#endif
 #ifndef SEPATTN_FIN_BLOCKS
 #define SEPATTN_FIN_BLOCKS 1024  // finalize workgroups in all (before the per-(b, kv head) floor of one)
 #endif
@@ -488,7 +504,9 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
 // ---------------------------------------------------------------------------
 // query-major dQ of one query tile over the forward's schedule
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// LEAN: fewer registers (the 32-key halves one after the other, K/V operands
+// read in groups of 4), for a kernel that runs two waves per SIMD at d=128
+template <typename T, int D, bool LEAN = false>
 __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, const SmemBufs<T>& sm) {
   typedef Traits<T> Tr;
   typedef TileGeom<T, D> G;
@@ -637,18 +655,23 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     // S^T = K Q^T and dP^T = V dO^T for the 32-key half k2 (operands first,
     // then the MFMAs back to back)
     auto scores = [&](int k2, f32x16& sacc, f32x16& pacc) {
-      frag kk[NQF], vv[NQF];
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        kk[c] = read_x<T, D>(K, k2, c, lane);
-        vv[c] = read_x<T, D>(V, k2, c, lane);
-      }
+      constexpr int GRP = LEAN && NQF > 4 ? 4 : NQF;  // operands read per group
       sacc = f32x16{};
-      pacc = negD;
+      if constexpr (LEAN) pacc = f32x16{};  // D subtracted per score below
+      else pacc = negD;
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        sacc = Tr::mfma(kk[c], qf[c], sacc);
-        pacc = Tr::mfma(vv[c], of[c], pacc);
+      for (int c0 = 0; c0 < NQF; c0 += GRP) {
+        frag kk[GRP], vv[GRP];
+#pragma unroll
+        for (int c = 0; c < GRP; ++c) {
+          kk[c] = read_x<T, D>(K, k2, c0 + c, lane);
+          vv[c] = read_x<T, D>(V, k2, c0 + c, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < GRP; ++c) {
+          sacc = Tr::mfma(kk[c], qf[c0 + c], sacc);
+          pacc = Tr::mfma(vv[c], of[c0 + c], pacc);
+        }
       }
     };
     // dS^T = P^T (dP^T - D) as MFMA operands (masked exponents become -inf, so P = 0)
@@ -661,24 +684,35 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
         for (int i = 0; i < 16; ++i) sacc[i] = keep_or_neg_inf(sacc[i], bit_mask(vw, acc_bit(i)));
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pacc[i] = fast_exp2(sacc[i]) * pacc[i];  // pacc holds dP^T - D
+      for (int i = 0; i < 16; ++i) pacc[i] = fast_exp2(sacc[i]) * (LEAN ? pacc[i] - Di : pacc[i]);  // dP^T - D
 #pragma unroll
       for (int sl = 0; sl < SPB; ++sl) sf[sl] = acc_frag<T>(pacc, sl);
     };
     // dQ^T += K^T dS^T with the K^T operands of the half read first
     auto dqmm = [&](int k2, const frag* sf) {
-      frag kt[SPB][NDB];
+      if constexpr (LEAN) {
 #pragma unroll
-      for (int sl = 0; sl < SPB; ++sl)
+        for (int sl = 0; sl < SPB; ++sl) {
+          frag kt[NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) kt[sl][db] = read_xt<T, D>(K, k2, sl, 32 * db, lane);
+          for (int db = 0; db < NDB; ++db) kt[db] = read_xt<T, D>(K, k2, sl, 32 * db, lane);
 #pragma unroll
-      for (int sl = 0; sl < SPB; ++sl)
+          for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[db], sf[sl], dq[db]);
+        }
+      } else {
+        frag kt[SPB][NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[sl][db], sf[sl], dq[db]);
+        for (int sl = 0; sl < SPB; ++sl)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) kt[sl][db] = read_xt<T, D>(K, k2, sl, 32 * db, lane);
+#pragma unroll
+        for (int sl = 0; sl < SPB; ++sl)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dq[db] = Tr::mfma(kt[sl][db], sf[sl], dq[db]);
+      }
     };
 
-    if (SEPATTN_DQ_INTERLEAVE && live[0] && live[1]) {
+    if (SEPATTN_DQ_INTERLEAVE && !LEAN && live[0] && live[1]) {
       // half 1's scores enter the MFMA pipe before half 0's dQ products, and
       // half 1's exponentials overlap those products
       f32x16 s0, p0, s1, p1;
@@ -780,6 +814,23 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, sm);
 }
 
+// dQ items in a kernel of their own (d=128: the main kernel's key-major items
+// hold more registers than two waves per SIMD allow; the dQ items alone fit)
+template <typename T, int D>
+__global__ void __launch_bounds__(kBwdThreads, D == 64 ? SEPATTN_DQ_SPLIT_OCC64 : SEPATTN_DQ_SPLIT_OCC) bwd_dq_kernel(BwdArgs p) {
+  typedef TileGeom<T, D> G;
+  __shared__ __attribute__((aligned(16))) T smA0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smA1[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smB0[G::ELEMS];
+  __shared__ __attribute__((aligned(16))) T smB1[G::ELEMS];
+  const SmemBufs<T> sm = {{smA0, smA1}, {smB0, smB1}, {nullptr, nullptr}};
+  const int x = blockIdx.x;
+  const int BH = p.B * p.Hq;
+  const int qi = p.QT - 1 - x / BH;
+  const int bh = x % BH;
+  dq_item<T, D, true>(p, bh / p.Hq, bh % p.Hq, qi, sm);
+}
+
 // ---------------------------------------------------------------------------
 // finalize: anchor rows = sum of their partial slots, stored in the input type
 // ---------------------------------------------------------------------------
@@ -847,15 +898,24 @@ static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   constexpr int TPR = D / Traits<T>::VEC;
   const size_t rows = (size_t)a.B * a.Hq * a.SB * kKTile;  // 64-padded rows
   const int pre_blocks = (int)((rows + kPreRows - 1) / kPreRows);
-  const int main_blocks = a.n_anchor_items + a.n_dq_items + a.n_band_items;
+  constexpr bool split = sizeof(T) == 2 && (D == 128 ? SEPATTN_DQ_SPLIT : SEPATTN_DQ_SPLIT64);
+  BwdArgs am = a;  // the main kernel's items (without the dQ items when they run apart)
+  if (split) am.n_dq_items = 0;
+  const int main_blocks = am.n_anchor_items + am.n_dq_items + am.n_band_items;
   const int fin_rows_per_block = 256 / (D / 4);
   hipError_t e;
   if (ev && ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_blocks), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, am);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (split) {
+    if (a.n_dq_items > 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.n_dq_items), dim3(kBwdThreads), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
   if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const int fin_x = std::max(1, std::min((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
                                          SEPATTN_FIN_BLOCKS / (a.B * a.Hkv)));
