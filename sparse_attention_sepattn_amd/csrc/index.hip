@@ -9,145 +9,185 @@
 // beiduofen.top, "Performance in the Spotlight"; atlas.scime.ai, "Surprising
 // findings"): with interval m > 0 the membership test is j % m == m - 1 and
 // no token ids are read; everything downstream is unchanged.
+//
+// One launch, one workgroup per (query tile, sequence).  A workgroup counts
+// the separators below its own tile itself (64-token blocks, one wave ballot
+// each), so no workgroup waits for another: the prefix work is redundant
+// across query tiles (the tokens stay in L2) but every workgroup starts at
+// once.  What it writes:
+//   * the schedule fields of its query tile and the class of every 128 x 64
+//     tile in its row of the grid: tiles left of every row's window from the
+//     block counts of the scan, tiles inside every row's window closed form,
+//     the few tiles that cross the diagonal or a window's left edge row by
+//     row from the block's 64-bit separator mask;
+//   * flags, prefix counts and anchor-list entries of its own 128 positions;
+//   * (last query tile) the totals and the -1 padding of the anchor list.
 #include "internal.hpp"
 
 namespace sepattn {
 
-#ifndef SEPATTN_SCAN_THREADS
-#define SEPATTN_SCAN_THREADS 1024
+#ifndef SEPATTN_INDEX_THREADS
+#define SEPATTN_INDEX_THREADS 1024
 #endif
-constexpr int kScanThreads = SEPATTN_SCAN_THREADS;
-constexpr int kScanItems = 8;  // consecutive tokens per thread per chunk
+constexpr int kIdxThreads = SEPATTN_INDEX_THREADS;
+constexpr int kIdxWaves = kIdxThreads / kWave;
+#ifndef SEPATTN_INDEX_BATCH
+#define SEPATTN_INDEX_BATCH 4
+#endif
+constexpr int kIdxBatch = SEPATTN_INDEX_BATCH;  // 64-token blocks per wave per pass
+static_assert(kKTile == kWave, "one lane per key of a 64-key block");
+static_assert(kQTile == 2 * kKTile, "a query tile spans two key blocks");
 
-// One workgroup per sequence.  Chunks of kScanThreads * kScanItems tokens are
-// scanned in order with a running carry, so the result is deterministic.
-__global__ void __launch_bounds__(kScanThreads)
-index_scan_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep, int interval,
-                  uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_prefix,
-                  int32_t* __restrict__ anchor_pos, int32_t* __restrict__ anchor_count) {
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const int wid = t / kWave;
-  constexpr int kWaves = kScanThreads / kWave;
-  __shared__ int wave_sum[kWaves];
-  __shared__ int carry_sh;
+// bits [0, k) of a 64-bit mask (k clamped to [0, 64])
+__device__ __forceinline__ uint64_t low_bits(int k) {
+  return k <= 0 ? 0ull : (k >= 64 ? ~0ull : ((1ull << k) - 1ull));
+}
 
-  const int32_t* tk = tok ? tok + (size_t)b * S : nullptr;
-  uint8_t* fl = is_sep + (size_t)b * S;
-  int32_t* pre = sep_prefix + (size_t)b * (S + 1);
-  int32_t* anc = anchor_pos + (size_t)b * S;
-  const int n_init = a < S ? a : S;
-
-  if (t == 0) carry_sh = 0;
-  __syncthreads();
-
-  for (int base = 0; base < S; base += kScanThreads * kScanItems) {
-    const int j0 = base + t * kScanItems;
-    // every token load is issued before any is used (clamped rows past S are
-    // read but not counted)
-    int32_t tv[kScanItems];
-    if (interval <= 0) {
+__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
-      for (int e = 0; e < kScanItems; ++e) tv[e] = tk[min(j0 + e, S - 1)];
-    }
-    // membership: ids outer, tokens inner, so each id is read once per chunk
-    bool hit[kScanItems];
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Anchor-candidate bit of position j (separator id, or on the interval); the
+// caller masks positions >= S.  `t` is the token at j (unused with an interval).
+__device__ __forceinline__ bool candidate(int32_t t, int j, const SepSet& sep, int interval) {
+  return interval > 0 ? j % interval == interval - 1 : is_separator(sep, t);
+}
+
+__global__ void __launch_bounds__(kIdxThreads)
+index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, int interval,
+             uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_prefix, int32_t* __restrict__ anchor_pos,
+             int32_t* __restrict__ anchor_count, int32_t* __restrict__ qtile, uint8_t* __restrict__ tile_class) {
+  const int QT = gridDim.x;
+  const int qi = QT - 1 - (int)blockIdx.x;  // the longest scans first
+  const int b = blockIdx.y;
+  const int KT = (S + kKTile - 1) / kKTile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int32_t* tk = tok ? tok + (size_t)b * S : nullptr;  // null with an interval
+  uint8_t* cls = tile_class + ((size_t)b * QT + qi) * KT;
+  const int q0 = qi * kQTile;
+  const int q1 = min(q0 + kQTile - 1, S - 1);
+  const int lo = max(0, q0 - n + 1);  // window start of the tile's first row
+  const bool last = qi == QT - 1;
+  const int n_init = min(a, S);
+  // tiles [0, k_far) end before every row's window (64 kj + 63 <= q0 - n):
+  // each row sees the same keys there, its initial tokens and separators
+  const int k_far = q0 - n - (kKTile - 1) >= 0 ? (q0 - n - (kKTile - 1)) / kKTile + 1 : 0;
+
+  // token loads of the later phases, issued before the scan so that their
+  // latency overlaps it: this wave's first row-by-row tile, and (waves 0, 1)
+  // the tile's own 128 positions.  Row-by-row tiles go to the waves from the
+  // last one down, which have the least scan work on short sequences.
+  const bool tok_ids = interval <= 0;
+  const int wr = kIdxWaves - 1 - w;
+  const int kj_first = k_far + wr;
+  int32_t t_row = 0, t_s0 = 0, t_s1 = 0;
+  if (tok_ids && kj_first <= q1 / kKTile) t_row = tk[min(kj_first * kKTile + lane, S - 1)];
+  if (tok_ids && w < kQTile / kKTile) {
+    t_s0 = tk[min(q0 + lane, S - 1)];
+    t_s1 = tk[min(q0 + kKTile + lane, S - 1)];
+  }
+
+  // (1) separators at [a, q0) and [a, lo) (all of [a, S) in the last tile),
+  // and the classes of the far-left tiles, block by block; the next pass's
+  // tokens are loaded while this pass is counted
+  const int nb = last ? KT : q0 / kKTile;
+  int s_q0 = 0, s_lo = 0, s_all = 0;  // wave-uniform
+  constexpr int kPass = kIdxWaves * kIdxBatch;
+  int32_t tv[kIdxBatch];
+  auto load_pass = [&](int base) {
 #pragma unroll
-    for (int e = 0; e < kScanItems; ++e) hit[e] = interval > 0 && (j0 + e) % interval == interval - 1;
-    if (interval <= 0) {
+    for (int e = 0; e < kIdxBatch; ++e) tv[e] = tk[min((base + e) * kKTile + lane, S - 1)];
+  };
+  if (tok_ids && w * kIdxBatch < nb) load_pass(w * kIdxBatch);
+  for (int base = w * kIdxBatch; base < nb; base += kPass) {
+    bool hit[kIdxBatch];
+    if (tok_ids) {
+#pragma unroll
+      for (int e = 0; e < kIdxBatch; ++e) hit[e] = false;
+      // ids outer, so each id is read once per pass
 #pragma unroll 4
       for (int i = 0; i < sep.n; ++i) {
         const int32_t id = sep.ids[i];
 #pragma unroll
-        for (int e = 0; e < kScanItems; ++e) hit[e] |= tv[e] == id;
+        for (int e = 0; e < kIdxBatch; ++e) hit[e] |= tv[e] == id;
+      }
+      if (base + kPass < nb) load_pass(base + kPass);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kIdxBatch; ++e) hit[e] = candidate(0, (base + e) * kKTile + lane, sep, interval);
+    }
+#pragma unroll
+    for (int e = 0; e < kIdxBatch; ++e) {
+      const int kj = base + e;
+      const int c0 = kj * kKTile;
+      const int j = c0 + lane;
+      // separators counted from position a on
+      const uint64_t m = __ballot(hit[e] && kj < nb && j < S && j >= a);
+      const int cnt = __popcll(m);
+      s_all += cnt;
+      s_q0 += __popcll(m & low_bits(q0 - c0));
+      s_lo += __popcll(m & low_bits(lo - c0));
+      if (kj < k_far && lane == 0) {
+        const int v = min(max(a - c0, 0), kKTile) + cnt;  // visible keys per row (full-width tile)
+        cls[kj] = v == 0 ? 0 : (v == kKTile ? 2 : 1);
       }
     }
-    int f[kScanItems];
-    int cnt = 0;
+  }
+  __shared__ int red[kIdxWaves][3];
+  if (lane == 0) {
+    red[w][0] = s_q0;
+    red[w][1] = s_lo;
+    red[w][2] = s_all;
+  }
+
+  // (2) classes of the tiles from k_far on: past the tile's last row 0,
+  // inside every row's window and causal range 2 (closed form, all threads);
+  // the rest row by row (one wave per tile)
+  for (int kj = k_far + (int)threadIdx.x; kj < KT; kj += kIdxThreads) {
+    const int c0 = kj * kKTile;
+    const int c1 = min(c0 + kKTile - 1, S - 1);
+    if (c0 > q1) cls[kj] = 0;
+    else if (c0 >= q1 - n + 1 && c1 <= q0) cls[kj] = 2;
+  }
+  for (int kj = kj_first; kj <= q1 / kKTile; kj += kIdxWaves) {
+    const int c0 = kj * kKTile;
+    const int c1 = min(c0 + kKTile - 1, S - 1);
+    if (c0 >= q1 - n + 1 && c1 <= q0) continue;  // written above
+    const int j = c0 + lane;
+    const int32_t t = !tok_ids ? 0 : (kj == kj_first ? t_row : tk[min(j, S - 1)]);
+    const uint64_t keep = __ballot(j <= c1 && candidate(t, j, sep, interval)) | low_bits(a - c0);
+    int total = 0;
 #pragma unroll
-    for (int e = 0; e < kScanItems; ++e) {
-      const int j = j0 + e;
-      const int s = hit[e] ? 1 : 0;
-      if (j < S) fl[j] = (uint8_t)s;
-      f[e] = (j < S && j >= a) ? s : 0;  // separators counted from position a on
-      cnt += f[e];
-    }
-    // inclusive scan of cnt across the wave
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    if (lane == kWave - 1) wave_sum[wid] = incl;
-    __syncthreads();
-    int wave_off = 0;
-    int chunk_total = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int ws = wave_sum[w];
-      wave_off += (w < wid) ? ws : 0;
-      chunk_total += ws;
-    }
-    const int carry = carry_sh;
-    int run = carry + wave_off + incl - cnt;  // exclusive prefix at j0
-#pragma unroll
-    for (int e = 0; e < kScanItems; ++e) {
-      const int j = j0 + e;
-      if (j < S) {
-        pre[j] = run;
-        if (j < n_init) anc[j] = j;
-        else if (f[e]) anc[n_init + run] = j;
+    for (int r = 0; r < kQTile / kWave; ++r) {
+      const int i = q0 + r * kWave + lane;
+      if (i <= q1) {
+        // keys of the tile row i sees: anchors or in its window, and j <= i
+        const uint64_t vis = (keep | ~low_bits(i - n + 1 - c0)) & low_bits(min(c1, i) - c0 + 1);
+        total += __popcll(vis);
       }
-      run += f[e];
     }
-    __syncthreads();
-    if (t == 0) carry_sh = carry + chunk_total;
-    __syncthreads();
+    total = wave_sum(total);
+    if (lane == 0) {
+      const int full = (q1 - q0 + 1) * (c1 - c0 + 1);
+      cls[kj] = total == 0 ? 0 : (total == full ? 2 : 1);
+    }
   }
-  const int total = carry_sh;
-  if (t == 0) {
-    pre[S] = total;
-    anchor_count[b] = n_init + total;
+
+  __syncthreads();
+  int pre_q0 = 0, pre_lo = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < kIdxWaves; ++v) {
+    pre_q0 += red[v][0];
+    pre_lo += red[v][1];
+    total += red[v][2];
   }
-  // pad the anchor list with -1
-  for (int j = n_init + total + t; j < S; j += kScanThreads) anc[j] = -1;
-}
 
-// Visible entries of the mask in row i over key columns [c0, c1] (c1 < S),
-// split so that a caller can keep many prefix loads in flight: `cnt` gets the
-// window and initial-token part, and the separator part is
-// pre[*hi_ix] - pre[*lo_ix] (both 0 when it is empty).
-__device__ __forceinline__ void row_count_parts(int i, int c0, int c1, int a, int n, int* cnt, int* hi_ix,
-                                                int* lo_ix) {
-  const int hi = c1 < i ? c1 : i;
-  const int w0 = (i - n + 1) > c0 ? (i - n + 1) : c0;
-  int c = hi >= w0 ? hi - w0 + 1 : 0;  // window part (empty when hi < c0)
-  const int e = hi < (i - n) ? hi : (i - n);  // last key outside the window
-  const int ie = e < a - 1 ? e : a - 1;
-  c += ie >= c0 ? ie - c0 + 1 : 0;  // initial tokens
-  const int s0 = c0 > a ? c0 : a;
-  const bool seps = e >= s0;  // separators in [s0, e]
-  *cnt = c;
-  *hi_ix = seps ? e + 1 : 0;
-  *lo_ix = seps ? s0 : 0;
-}
-
-// Grid (QT, B): per query tile, its schedule fields and the class of every
-// 128 x 64 tile in its row of the grid.
-__global__ void __launch_bounds__(256)
-index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
-                   int32_t* __restrict__ qtile, uint8_t* __restrict__ tile_class) {
-  const int qi = blockIdx.x;
-  const int b = blockIdx.y;
-  const int QT = gridDim.x;
-  const int KT = (S + kKTile - 1) / kKTile;
-  const int32_t* pre = sep_prefix + (size_t)b * (S + 1);
-  const int q0 = qi * kQTile;
-  const int q1 = min(q0 + kQTile - 1, S - 1);
+  // (3) schedule fields of the query tile
   if (threadIdx.x == 0) {
-    const int lo = max(0, q0 - n + 1);
-    const int n_anchor = min(a, lo) + pre[lo];
+    const int n_anchor = min(a, lo) + pre_lo;
     const int kb = lo / kKTile;
     const int ke = q1 / kKTile;
     int32_t* f = qtile + ((size_t)b * QT + qi) * kQF;
@@ -160,63 +200,45 @@ index_tiles_kernel(int S, int a, int n, const int32_t* __restrict__ sep_prefix,
     f[6] = q0;
     f[7] = 0;
   }
-  // 8 lanes per key tile, each counting 16 of the 128 rows
-  uint8_t* cls = tile_class + ((size_t)b * QT + qi) * KT;
-  const int sub = threadIdx.x & 7;
-  for (int base = 0; base < KT; base += blockDim.x / 8) {
-    const int kj = base + threadIdx.x / 8;
-    const int c0 = kj * kKTile;
-    const int c1 = min(c0 + kKTile - 1, S - 1);
-    int total = 0;
-    if (kj < KT && c0 <= q1) {
-      if (c1 <= q0 - n) {
-        // left of every row's window: each row sees the same keys of the
-        // tile (its initial tokens and separators), so count one row
-        if (sub == 0) {
-          int c, hx, lx;
-          row_count_parts(q0, c0, c1, a, n, &c, &hx, &lx);
-          total = (q1 - q0 + 1) * (c + pre[hx] - pre[lx]);
-        }
-      } else {
-        // the 16 rows of this lane (rows past the tile are not counted), all
-        // of their prefix loads issued before any is used
-        constexpr int R = kQTile / 8;
-        int c[R], hx[R], lx[R], ph[R], pl[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int i = q0 + sub + 8 * r;
-          row_count_parts(min(i, q1), c0, c1, a, n, &c[r], &hx[r], &lx[r]);
-          if (i > q1) c[r] = hx[r] = lx[r] = 0;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          ph[r] = pre[hx[r]];
-          pl[r] = pre[lx[r]];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < R; ++r) total += c[r] + ph[r] - pl[r];
-      }
+
+  // (4) flags, prefix counts and anchor entries of positions [q0, q1]: wave 0
+  // the first 64, wave 1 the second (both need the first block's count)
+  int32_t* pre = sep_prefix + (size_t)b * (S + 1);
+  int32_t* anc = anchor_pos + (size_t)b * S;
+  if (w < kQTile / kKTile && q0 + w * kKTile < S) {
+    const int j0 = q0 + lane;
+    const int j1 = q0 + kKTile + lane;
+    const uint64_t raw0 = __ballot(j0 < S && candidate(t_s0, j0, sep, interval));
+    const uint64_t raw1 = __ballot(j1 < S && candidate(t_s1, j1, sep, interval));
+    const uint64_t cnt0 = raw0 & ~low_bits(a - q0);
+    const uint64_t cnt1 = raw1 & ~low_bits(a - q0 - kKTile);
+    const uint64_t raw = w ? raw1 : raw0;
+    const uint64_t cm = w ? cnt1 : cnt0;
+    const int j = w ? j1 : j0;
+    if (j < S) {
+      const int pj = pre_q0 + (w ? __popcll(cnt0) : 0) + __popcll(cm & low_bits(lane));
+      is_sep[(size_t)b * S + j] = (uint8_t)((raw >> lane) & 1ull);
+      pre[j] = pj;
+      if (j < n_init) anc[j] = j;
+      else if ((cm >> lane) & 1ull) anc[n_init + pj] = j;
     }
-    total += __shfl_xor(total, 1, 64);
-    total += __shfl_xor(total, 2, 64);
-    total += __shfl_xor(total, 4, 64);
-    if (kj < KT && sub == 0) {
-      const int full = (q1 - q0 + 1) * (c1 - c0 + 1);
-      cls[kj] = total == 0 ? 0 : (total == full ? 2 : 1);
+  }
+
+  // (5) totals and the anchor list's padding
+  if (last) {
+    if (threadIdx.x == 0) {
+      pre[S] = total;
+      anchor_count[b] = n_init + total;
     }
+    for (int j = n_init + total + (int)threadIdx.x; j < S; j += kIdxThreads) anc[j] = -1;
   }
 }
 
 hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int interval, int a, int n,
                               const sepattn_index& idx, hipStream_t stream) {
-  hipLaunchKernelGGL(index_scan_kernel, dim3(B), dim3(kScanThreads), 0, stream, tok, S, a, sep, interval,
-                     idx.is_sep, idx.sep_prefix, idx.anchor_pos, idx.anchor_count);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int QT = (S + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(index_tiles_kernel, dim3(QT, B), dim3(256), 0, stream, S, a, n,
-                     idx.sep_prefix, idx.qtile, idx.tile_class);
+  hipLaunchKernelGGL(index_kernel, dim3(QT, B), dim3(kIdxThreads), 0, stream, tok, S, a, n, sep, interval,
+                     idx.is_sep, idx.sep_prefix, idx.anchor_pos, idx.anchor_count, idx.qtile, idx.tile_class);
   return hipGetLastError();
 }
 
