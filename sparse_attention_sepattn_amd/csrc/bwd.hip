@@ -37,7 +37,10 @@ namespace sepattn {
 
 constexpr int kBwdThreads = 256;
 constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
-constexpr int kPreRows = 128;    // rows of D per workgroup of the pre kernel
+#ifndef SEPATTN_PRE_ROWS
+#define SEPATTN_PRE_ROWS 64
+#endif
+constexpr int kPreRows = SEPATTN_PRE_ROWS;  // rows of D per workgroup of the pre kernel
 
 // Workgroups per CU the register budget of the main kernel targets: the
 // d=128 and fp32 kernels keep more operands resident (key fragments and
