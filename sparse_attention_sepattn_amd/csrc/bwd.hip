@@ -237,7 +237,7 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tests on it are scalar branches
   const int hh = lane >> 5;
   const int kc = lane & 31;
   const int grp = p.Hq / p.Hkv;
@@ -524,7 +524,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tests on it are scalar branches
   const int hh = lane >> 5;
   const int qc = lane & 31;
   const int g = h / (p.Hq / p.Hkv);
