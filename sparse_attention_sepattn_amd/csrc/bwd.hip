@@ -15,7 +15,9 @@
 //     anchor dK/dV -- key-major over gathered anchor tiles (128 anchors per
 //              workgroup); the query tiles are split into chunks and each
 //              (anchor tile, chunk) stores its fp32 partial in its own slot;
-//     dQ       -- query-major over the forward's schedule;
+//     dQ       -- query-major over the forward's schedule (bf16 at d=128:
+//              in a kernel of their own right after the main one, which fits
+//              two waves per SIMD where the key-major items fit one);
 //     band dK/dV -- key-major over 128-key tiles of the local band; a
 //              workgroup owns its rows: rows that are not anchors seen through
 //              the anchor path are scaled and stored in the input type, the
