@@ -148,3 +148,36 @@ def test_bwd_long_context_sampled():
             rmax, rfro = _rel(got, ref)
             say(f"  32k {name} kv head {g}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
             assert rmax <= 3e-2 and rfro <= 1e-2
+
+
+def test_bwd_llama_config_sampled():
+    """Llama-3-8B-shaped prefill (S 8192, 32 q / 8 kv heads, d128, n 256):
+    dQ on sampled rows of heads 0, 13 and 31; dK/dV on key rows sampled over
+    the whole sequence -- the initial tokens, the first and last separators
+    (anchors whose gradients collect every later query row, over several
+    anchor chunks) and every 97th row -- of kv heads 0 and 7."""
+    require_gpu()
+    cfg = synth.CONFIGS["llama3_8b_prefill"]
+    inp = synth.prefill_inputs(cfg, with_grad=True)
+    dq, dk, dv = _gpu_grads(inp)
+    S, grp = cfg["S"], cfg["Hq"] // cfg["Hkv"]
+    sepf = sepmask.separator_flags(inp["tok"][0], inp["sep"])
+    rows = np.unique(np.concatenate([np.arange(0, S, 211), np.arange(S - 40, S), np.arange(0, 40)]))
+    for h in (0, 13, 31):
+        g = h // grp
+        ref = attention.grad_q_rows(inp["qf"][0, h], inp["kf"][0, g], inp["vf"][0, g], inp["dof"][0, h],
+                                    sepf, cfg["a"], cfg["n"], inp["scale"], rows)
+        rmax, rfro = _rel(dq[0, h, rows], ref)
+        say(f"  llama dq head {h}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+        assert rmax <= 3e-2 and rfro <= 1e-2
+    seps = np.nonzero(sepf)[0]
+    cols = np.unique(np.concatenate([np.arange(0, S, 97), np.arange(0, 70), seps[:40], seps[-40:]]))
+    for g in (0, 7):
+        hs = range(g * grp, (g + 1) * grp)
+        rk, rv = attention.grad_kv_cols([inp["qf"][0, h] for h in hs], inp["kf"][0, g], inp["vf"][0, g],
+                                        [inp["dof"][0, h] for h in hs], sepf, cfg["a"], cfg["n"],
+                                        inp["scale"], cols)
+        for name, got, ref in (("dk", dk[0, g, cols], rk), ("dv", dv[0, g, cols], rv)):
+            rmax, rfro = _rel(got, ref)
+            say(f"  llama {name} kv head {g}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+            assert rmax <= 3e-2 and rfro <= 1e-2
