@@ -124,7 +124,9 @@ int sepattn_index_bind(void* buf, size_t bytes, int B, int S, sepattn_index* idx
  * separator id set `sep_ids` (HOST array of n_sep int32, 0 <= n_sep <=
  * SEPATTN_MAX_SEP_IDS, read before the call returns), `a` initial tokens
  * (a >= 0) and window `n` (n >= 1).  idx must have been bound for the same
- * B and S; idx->a and idx->n are set.  Every output field is written. */
+ * B and S; idx->a and idx->n are set, idx->n to min(n, S) (every n >= S
+ * gives the same mask; sepattn_fwd and sepattn_bwd apply the same bound to
+ * an idx->n set by hand).  Every output field is written. */
 int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* sep_ids, int n_sep,
                         int a, int n, sepattn_index* idx, void* stream);
 

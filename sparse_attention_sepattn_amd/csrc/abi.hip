@@ -115,7 +115,7 @@ int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* s
   int st = make_sepset(sep_ids, n_sep, &sep);
   if (st != SEPATTN_OK) return st;
   idx->a = a;
-  idx->n = n;
+  idx->n = n = n < S ? n : S;  // any n >= S keeps every j <= i: the same mask, no overflow in n-arithmetic
   forget_stale_error();
   return to_status(launch_build_index(token_ids, B, S, sep, 0, a, n, *idx, (hipStream_t)stream));
 }
@@ -128,7 +128,7 @@ int sepattn_build_index_interval(int B, int S, int interval, int a, int n, sepat
   SepSet none;
   memset(&none, 0, sizeof(none));
   idx->a = a;
-  idx->n = n;
+  idx->n = n = n < S ? n : S;
   forget_stale_error();
   return to_status(launch_build_index(nullptr, B, S, none, interval, a, n, *idx, (hipStream_t)stream));
 }

@@ -963,7 +963,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.Hkv = sh.Hkv;
   a.S = sh.S;
   a.a = idx.a;
-  a.n = idx.n;
+  a.n = idx.n < idx.S ? idx.n : idx.S;  // as the index builders store it
   a.units = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
   a.anchor_lanes = std::min(a.units, std::max(2, sh.S / 2048));
   a.n_anchor_items = a.anchor_lanes * sh.B * sh.Hkv * a.nchunk;

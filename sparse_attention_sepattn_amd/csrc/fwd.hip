@@ -342,7 +342,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const AttnSha
   a.Hkv = sh.Hkv;
   a.S = sh.S;
   a.a = idx.a;
-  a.n = idx.n;
+  a.n = idx.n < idx.S ? idx.n : idx.S;  // as the index builders store it
   a.QT = (sh.S + kQTile - 1) / kQTile;
   a.scale_log2 = sh.scale * 1.4426950408889634f;
   if (sh.dtype == SEPATTN_BF16) {

@@ -72,6 +72,8 @@ CASES = [
     (1000, 1, 2, 2, 64, "bf16", 0, 1, 0.0),
     (640, 1, 2, 1, 128, "bf16", 4, 40, 1.0),
     (2500, 1, 2, 1, 64, "f32", 4, 64, 0.08),
+    (300, 1, 2, 1, 64, "bf16", 4, 2**31 - 1, 0.1),  # window beyond S: dense causal, no overflow
+    (200, 1, 2, 2, 64, "bf16", 2**31 - 1, 8, 0.1),  # every token initial
 ]
 
 

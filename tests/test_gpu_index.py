@@ -35,7 +35,8 @@ def _check(tok, sep, a, n):
                                      (129, 4, 64, 0.08), (300, 0, 1000, 0.2), (1000, 7, 100, 0.0),
                                      (1000, 4, 64, 1.0), (8193, 4, 256, 0.08), (700, 100, 64, 0.1),
                                      (200, 300, 5, 0.2), (2049, 4, 2049, 0.08), (1500, 70, 130, 0.05),
-                                     (777, 64, 63, 0.3), (1025, 1, 1, 0.9)])
+                                     (777, 64, 63, 0.3), (1025, 1, 1, 0.9), (300, 4, 2**31 - 1, 0.1),
+                                     (500, 2**31 - 1, 5, 0.1)])
 def test_index_small_and_ragged(S, a, n, p):
     require_gpu()
     r = synth.rng(S + a + n)
