@@ -38,6 +38,8 @@ int check_attn(int B, int Hq, int Hkv, int S, int d, int dtype, float scale) {
     return SEPATTN_EINVAL;
   if (dtype != SEPATTN_F32 && dtype != SEPATTN_BF16) return SEPATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return SEPATTN_EUNSUPPORTED;
+  // one (sequence, head) slice is addressed through 32-bit buffer offsets
+  if ((long long)S * d * (dtype == SEPATTN_F32 ? 4 : 2) >= (1ll << 31)) return SEPATTN_EUNSUPPORTED;
   return SEPATTN_OK;
 }
 

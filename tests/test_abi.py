@@ -65,6 +65,10 @@ def test_argument_errors_are_host_side():
     assert L.sepattn_fwd(z, fake, fake, 1, 2, 1, 64, 64, 1, 0.1, ctypes.byref(st), fake, fake, z) == 1
     # index bound for another shape
     assert L.sepattn_fwd(fake, fake, fake, 1, 2, 1, 128, 64, 1, 0.1, ctypes.byref(st), fake, fake, z) == 1
+    # a (sequence, head) slice of 2^31 bytes or more (32-bit buffer offsets)
+    assert L.sepattn_fwd(fake, fake, fake, 1, 2, 1, 1 << 23, 128, 1, 0.1, ctypes.byref(st), fake, fake, z) == 2
+    assert L.sepattn_bwd_workspace(1, 2, 1, 1 << 23, 128, 1) == 0
+    assert L.sepattn_bwd_workspace(1, 2, 1, (1 << 23) - 1, 128, 1) > 0
     # build_index: n < 1, a < 0, too many separator ids
     ids = (ctypes.c_int32 * 65)(*range(65))
     assert L.sepattn_build_index(fake, 1, 64, ids, 3, 4, 0, ctypes.byref(st), z) == 1
