@@ -53,8 +53,10 @@ extern "C" {
 /* status codes */
 #define SEPATTN_OK 0
 #define SEPATTN_EINVAL 1       /* null pointer, negative or zero size, a < 0, n < 1, Hq % Hkv != 0, scale <= 0, ... */
-#define SEPATTN_EUNSUPPORTED 2 /* dtype / head-dim combination not built (d must be 64 or 128), or one
-                                  (sequence, head) slice S*d*element size at or above 2^31 bytes */
+#define SEPATTN_EUNSUPPORTED 2 /* dtype / head-dim combination not built (d must be 64 or 128); one
+                                  (sequence, head) slice S*d*element size at or above 2^31 bytes;
+                                  more than 65535 query tiles of 128 rows, batch entries, or
+                                  batch x kv-head pairs (launch grid dimensions) */
 #define SEPATTN_ECAPACITY 3    /* SepCache capacities: need w >= 1, s >= 0, a >= 0 and c > a + s + w */
 #define SEPATTN_EWORKSPACE 4   /* workspace smaller than the matching *_workspace() query */
 #define SEPATTN_EHIP 5         /* a HIP launch failed */

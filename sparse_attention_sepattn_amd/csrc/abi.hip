@@ -38,15 +38,17 @@ int check_attn(int B, int Hq, int Hkv, int S, int d, int dtype, float scale) {
     return SEPATTN_EINVAL;
   if (dtype != SEPATTN_F32 && dtype != SEPATTN_BF16) return SEPATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return SEPATTN_EUNSUPPORTED;
-  // one (sequence, head) slice is addressed through 32-bit buffer offsets
+  // one (sequence, head) slice is addressed through 32-bit buffer offsets;
+  // query tiles and (sequence, kv head) pairs are grid dimensions (<= 65535)
   if ((long long)S * d * (dtype == SEPATTN_F32 ? 4 : 2) >= (1ll << 31)) return SEPATTN_EUNSUPPORTED;
+  if (S > kMaxGridDim * kQTile || (long long)B * Hkv > kMaxGridDim) return SEPATTN_EUNSUPPORTED;
   return SEPATTN_OK;
 }
 
 int check_cache(const sepcache* c) {
   if (!c || !c->k || !c->v || !c->pos || !c->tok || !c->state) return SEPATTN_EINVAL;
   if (c->B < 1 || c->Hkv < 1) return SEPATTN_EINVAL;
-  if (c->Hkv > kMaxCacheHeads) return SEPATTN_EUNSUPPORTED;
+  if (c->Hkv > kMaxCacheHeads || c->B > kMaxGridDim) return SEPATTN_EUNSUPPORTED;
   if (c->d != 64 && c->d != 128) return SEPATTN_EUNSUPPORTED;
   if (c->a < 0 || c->s < 0 || c->w < 1) return SEPATTN_ECAPACITY;
   if ((long long)c->c <= (long long)c->a + c->s + c->w) return SEPATTN_ECAPACITY;
@@ -110,6 +112,7 @@ int sepattn_index_bind(void* buf, size_t bytes, int B, int S, sepattn_index* idx
 int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* sep_ids, int n_sep,
                         int a, int n, sepattn_index* idx, void* stream) {
   if (!token_ids || !idx || B < 1 || S < 1 || a < 0 || n < 1) return SEPATTN_EINVAL;
+  if (B > kMaxGridDim) return SEPATTN_EUNSUPPORTED;
   if (idx->B != B || idx->S != S || !idx->is_sep || !idx->sep_prefix || !idx->anchor_pos ||
       !idx->anchor_count || !idx->qtile || !idx->tile_class)
     return SEPATTN_EINVAL;
@@ -124,6 +127,7 @@ int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* s
 
 int sepattn_build_index_interval(int B, int S, int interval, int a, int n, sepattn_index* idx, void* stream) {
   if (!idx || B < 1 || S < 1 || interval < 1 || a < 0 || n < 1) return SEPATTN_EINVAL;
+  if (B > kMaxGridDim) return SEPATTN_EUNSUPPORTED;
   if (idx->B != B || idx->S != S || !idx->is_sep || !idx->sep_prefix || !idx->anchor_pos ||
       !idx->anchor_count || !idx->qtile || !idx->tile_class)
     return SEPATTN_EINVAL;

@@ -12,6 +12,8 @@ constexpr int kMaxCacheCapacity = 8192;
 constexpr int kMaxCacheHeads = 128;
 // Largest number of query heads per kv head in decode.
 constexpr int kMaxDecodeGroup = 8;
+// grid y / z dimensions a launch may use (batch, query tiles, batch x kv heads)
+constexpr int kMaxGridDim = 65535;
 
 hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int interval, int a, int n,
                               const sepattn_index& idx, hipStream_t stream);

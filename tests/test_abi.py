@@ -68,12 +68,18 @@ def test_argument_errors_are_host_side():
     # a (sequence, head) slice of 2^31 bytes or more (32-bit buffer offsets)
     assert L.sepattn_fwd(fake, fake, fake, 1, 2, 1, 1 << 23, 128, 1, 0.1, ctypes.byref(st), fake, fake, z) == 2
     assert L.sepattn_bwd_workspace(1, 2, 1, 1 << 23, 128, 1) == 0
-    assert L.sepattn_bwd_workspace(1, 2, 1, (1 << 23) - 1, 128, 1) > 0
+    assert L.sepattn_bwd_workspace(1, 2, 1, (1 << 23) - 1, 128, 0) == 0  # fp32: 2^31 bytes at 2^22 rows
+    assert L.sepattn_bwd_workspace(1, 2, 1, 65535 * 128, 128, 1) > 0
+    # launch grid dimensions: query tiles, batch x kv heads, batch of the index
+    assert L.sepattn_bwd_workspace(1, 2, 1, 65535 * 128 + 1, 64, 1) == 0
+    assert L.sepattn_bwd_workspace(65536, 2, 1, 64, 64, 1) == 0
+    assert L.sepattn_bwd_workspace(32768, 4, 2, 64, 64, 1) == 0
     # build_index: n < 1, a < 0, too many separator ids
     ids = (ctypes.c_int32 * 65)(*range(65))
     assert L.sepattn_build_index(fake, 1, 64, ids, 3, 4, 0, ctypes.byref(st), z) == 1
     assert L.sepattn_build_index(fake, 1, 64, ids, 3, -1, 4, ctypes.byref(st), z) == 1
     assert L.sepattn_build_index(fake, 1, 64, ids, 65, 4, 4, ctypes.byref(st), z) == 1
+    assert L.sepattn_build_index(fake, 65536, 64, ids, 3, 4, 4, ctypes.byref(st), z) == 2  # grid dimension
     # fixed-interval index: interval < 1, index bound for another shape
     assert L.sepattn_build_index_interval(1, 64, 0, 4, 4, ctypes.byref(st), z) == 1
     assert L.sepattn_build_index_interval(1, 128, 12, 4, 4, ctypes.byref(st), z) == 1
@@ -102,6 +108,9 @@ def test_cache_capacity_errors():
     assert L.sepcache_init(ctypes.byref(c), z) == 3          # w < 1
     c.w, c.d = 256, 96
     assert L.sepcache_init(ctypes.byref(c), z) == 2          # head dim
+    c.d, c.B = 128, 65536
+    assert L.sepcache_init(ctypes.byref(c), z) == 2          # batch beyond a grid dimension
+    c.B = 2
     # prefill hand-off: index of another shape or another `a`, P < 1 (all
     # rejected on the host before any launch)
     c.d = 128
