@@ -256,7 +256,10 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     const int first = p0 >= 0 ? (p0 + p.n - 1) / kQTile + 1 : p.QT;
     if (first >= p.QT) return false;  // no query sees these anchors (nor later ones); never read
     qi_begin = max(first, chunk * p.chunk_tiles);
-    qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);  // may be empty: the slot is then zero-filled
+    qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);
+    // no query tile of this chunk sees the unit: nothing to add, and the
+    // finalize never reads this chunk's slot for these anchors
+    if (qi_begin >= qi_end) return true;
   } else {
     const int k0 = unit * kKeysPerWG;
     const int k1 = min(k0 + kKeysPerWG - 1, p.S - 1);
@@ -852,10 +855,15 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdArgs p) {
   for (int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR; ai < n_last; ai += gridDim.x * (256 / TPR)) {
     const size_t off = ((size_t)bg * p.S + ai) * D + c4;
     const int krow = p.anchor_pos[(size_t)b * p.S + ai];
+    // the anchor-path chunks that hold a query tile seeing this anchor (the
+    // first such tile is the first whose window starts after it; earlier
+    // chunks' slots were not written), then the band slot
+    const int first = (krow + p.n - 1) / kQTile + 1;
+    const int cmin = min(first / p.chunk_tiles, p.nchunk);
     f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
     // the partials of 4 slots in flight at once (slots past nchunk re-read
     // the last one and are not added)
-    for (int c0 = 0; c0 <= p.nchunk; c0 += 4) {
+    for (int c0 = cmin; c0 <= p.nchunk; c0 += 4) {
       f32x4 k4[4], v4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
