@@ -2,8 +2,9 @@
 // over the kept tiles of each 128-row query tile -- the key tiles
 // kt_begin..kt_end of the local band (masked element-wise), then
 // ceil(n_anchor/64) tiles of gathered anchors (initial tokens and separators
-// below the window, visible to every row of the tile, so unmasked).  Online softmax in the base-2 domain,
-// fp32 accumulation, P rounded to the input type for the second product.
+// below the window, visible to every row of the tile, so unmasked).  Online
+// softmax in the base-2 domain, fp32 accumulation, P rounded to the input
+// type for the second product.
 //
 // Mask: SepLLM summary on atlas.scime.ai, "Approach".  Output O = M(A, V, M_b)
 // read as softmax renormalised over the kept keys ("How SepLLM Reorchestrates
@@ -35,7 +36,7 @@ constexpr float kLazy = 8.f;
 #define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
 #endif
 #ifndef SEPATTN_FWD_OCC
-#define SEPATTN_FWD_OCC 3  // workgroups per CU the bf16 d=64 register budget targets (4 spills)
+#define SEPATTN_FWD_OCC 3  // workgroups per CU the bf16 d=64 register budget targets (4 spills at 4)
 #endif
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
