@@ -39,8 +39,10 @@ over the steady state (steps 1024..4095), counting every cached K/V row read
 once per step per kv head plus the queries.
 
 cpu_baseline: the fp64 CPU oracle (plain numpy, materialised mask) timed on a
-bounded sample of the same workload (the first heads of sequence 0), scaled
-to the same unit.
+bounded sample of the same workload (whole sequences, all heads, until about
+--cpu-seconds of work or the whole batch), scaled to the same unit, with the
+thread count numpy's BLAS used; beside it the same oracle on one thread for
+sequence 0.
 """
 
 import argparse
@@ -552,10 +554,25 @@ def cpu_leg(args, inp, E_seqs):
         nb += 1
         if spent >= args.cpu_seconds:
             break
-    return dict(value=round(flops / spent / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"fp64 numpy oracle fwd+bwd of sequences 0..{nb - 1}, all {Hq} heads, of the same inputs "
-                       f"({nb * Hq} of {cfg['B'] * Hq} (sequence, head) pairs), {spent:.1f} s",
-                seconds=round(spent, 2))
+    out = dict(value=round(flops / spent / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+               sample=f"fp64 numpy oracle fwd+bwd of sequences 0..{nb - 1}, all {Hq} heads, of the same inputs "
+                      f"({nb * Hq} of {cfg['B'] * Hq} (sequence, head) pairs), {spent:.1f} s",
+               seconds=round(spent, 2))
+    try:  # the same oracle on one thread, sequence 0
+        from threadpoolctl import threadpool_limits
+        sl = (slice(0, 1), slice(0, Hq))
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            attention.attention_forward(inp["qf"][sl], inp["kf"][sl], inp["vf"][sl], inp["tok"][0:1], inp["sep"],
+                                        a, n, scale=inp["scale"])
+            attention.attention_backward(inp["qf"][sl], inp["kf"][sl], inp["vf"][sl], inp["dof"][sl],
+                                         inp["tok"][0:1], inp["sep"], a, n, scale=inp["scale"])
+            t1 = time.perf_counter() - t
+        out["single_thread"] = dict(value=round((4 + 10) * d * E_seqs[0] * Hq / t1 / 1e12, 6), unit="TFLOP/s",
+                                    cores=1, sample=f"sequence 0, all {Hq} heads, {t1:.1f} s")
+    except ImportError:
+        pass
+    return out
 
 
 def main():
