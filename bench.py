@@ -319,6 +319,39 @@ def dense_layer(args, torch, sa, tensors, tok, sep, scale, cfg, ev_cls):
                 causal_TFLOPs=round(14 * d * causal / (ms * 1e-3) / 1e12, 3))
 
 
+def tiny_config(torch, sa, synth, calls=50):
+    """The fp32 parity configuration (B1 H1 S512 d64, forward only): a
+    latency figure, the median over `calls` event-timed launches of the
+    index and of the forward."""
+    cfg = synth.CONFIGS["tiny_fp32"]
+    B, Hq, Hkv, S, d, a, n = (cfg[x] for x in ("B", "Hq", "Hkv", "S", "d", "a", "n"))
+    inp = synth.prefill_inputs(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[x], dtype=np.float32)).to(dev) for x in ("q", "k", "v"))
+    tok = torch.from_numpy(inp["tok"]).to(dev)
+    idx = sa.Index(B, S, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    ev = Events()
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(5):
+        sa.build_index(tok, inp["sep"], a, n, index=idx)
+        sa.fwd(q, k, v, idx, inp["scale"], o=o, lse=lse)
+    marks = [ev.new(3) for _ in range(calls)]
+    for m in marks:
+        ev.record(m[0], stream)
+        sa.build_index(tok, inp["sep"], a, n, index=idx)
+        ev.record(m[1], stream)
+        sa.fwd(q, k, v, idx, inp["scale"], o=o, lse=lse)
+        ev.record(m[2], stream)
+    torch.cuda.synchronize()
+    t_idx = float(np.median([ev.ms(m[0], m[1]) for m in marks])) * 1e3
+    t_fwd = float(np.median([ev.ms(m[1], m[2]) for m in marks])) * 1e3
+    ev.close()
+    return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, a=a, n=n, dtype="f32", calls=calls,
+                index_us=round(t_idx, 2), fwd_us=round(t_fwd, 2))
+
+
 def long_configs(args, torch, sa, synth):
     """The d=128 prefill/training shapes (Llama-3-8B-shaped prefill at 8192
     tokens, and 32768 tokens with bursty separators): whole steps (index,
@@ -619,6 +652,8 @@ def main():
         result["other_configs"] = long_configs(args, torch, sa, synth)
         for nm, r in result["other_configs"].items():
             log(f"  {nm}: {r['ms_per_step']} ms/step, forward {r['fwd_ms']} ms = {r['fwd_TFLOPs']} TFLOP/s")
+        result["other_configs"]["tiny_fp32"] = tiny = tiny_config(torch, sa, synth)
+        log(f"  tiny_fp32: index {tiny['index_us']} us, forward {tiny['fwd_us']} us")
     if not args.no_decode:
         log("decode leg ...")
         result["decode"] = decode_leg(args, torch, sa, synth)
