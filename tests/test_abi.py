@@ -137,3 +137,18 @@ def test_rope_table_host_matches_double_precision():
     f = theta ** (-2.0 * np.arange(d // 2) / d)
     assert np.array_equal(cos, np.cos(p * f).astype(np.float32))
     assert np.array_equal(sin, np.sin(p * f).astype(np.float32))
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU path: every entry point of the binding raises on host tensors
+    before anything reaches the library."""
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    tok = torch.zeros((1, 64), dtype=torch.int32)
+    with pytest.raises(TypeError, match="CUDA"):
+        sa.build_index(tok, [1, 2], 4, 8)
+    with pytest.raises(TypeError, match="CUDA"):
+        sa.fwd(q, k, k, None)
+    with pytest.raises(TypeError, match="CUDA"):
+        sa.bwd(q, k, k, q, torch.zeros((1, 2, 64)), q, None)
