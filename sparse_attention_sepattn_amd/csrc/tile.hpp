@@ -59,13 +59,16 @@ struct Traits<float> {
 __device__ __forceinline__ int acc_row(int i, int hh) { return ((i >> 2) << 3) + (hh << 2) + (i & 3); }
 
 // 16-byte chunks of a row are stored XOR-swizzled by the row index (no
-// padding).  The row-major read of 32 consecutive rows at one chunk and the
-// transpose read of 4 consecutive rows x 32 bytes both touch distinct banks:
-//   >= 16 chunks per row: c ^ f(r), f bijective on r % 16, and the 4 rows of
-//   an aligned group map a chunk pair {2k, 2k+1} to 8 distinct chunks;
+// padding).  The row-major read of 16 consecutive rows at one chunk (one
+// 256-byte LDS phase) touches distinct banks:
+//   >= 16 chunks per row: c ^ f(r), f bijective on r % 16;
 //   8 chunks per row (two rows per 256-byte bank line): c ^ g(r) with g
-//   bijective on (r >> 1) % 8 and rows r, r+2 of an aligned group differing
-//   in a bit >= 1.
+//   bijective on (r >> 1) % 8.
+// The transpose read (32 lanes x 8 bytes = 4 rows x 64 bytes per phase) meets
+// 2-way conflicts on two of its rows.  A swizzle free of them for both reads
+// exists (XOR on the higher chunk bits), but it no longer commutes with the
+// constant chunk offsets of the read sites, so every site needs its own
+// address register; measured, that cost more than the conflicts.
 __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
 __device__ __forceinline__ int swz8(int r) {
   const int x = (r >> 1) & 7;
