@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["Index", "SepCache", "build_index", "fwd", "bwd", "rope_table", "load_library",
+__all__ = ["Index", "SepCache", "build_index", "fwd", "bwd", "attention", "rope_table", "load_library",
            "SepattnError", "QTILE", "KTILE", "QTILE_FIELDS"]
 
 QTILE = 128
@@ -262,6 +262,33 @@ def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(L.sepattn_bwd_profiled(*args, arr, len(events)), "bwd_profiled")
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """fwd in forward, bwd in backward (the saved O and LSE are the
+    forward's, as in training)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, index, scale):
+        o, lse = fwd(q, k, v, index, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.index, ctx.scale = index, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.index, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, index, scale=None):
+    """SepLLM attention of q [B,Hq,S,d] over k/v [B,Hkv,S,d] under ``index``
+    (from build_index), differentiable through torch.autograd: the forward
+    and the backward are the library's kernels."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _Attention.apply(q, k, v, index, float(scale))
 
 
 def rope_table(theta, c, d):

@@ -186,3 +186,23 @@ def test_bwd_llama_config_sampled():
             rmax, rfro = _rel(got, ref)
             say(f"  llama {name} kv head {g}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
             assert rmax <= 3e-2 and rfro <= 1e-2
+
+
+def test_autograd_function_matches_direct_calls():
+    """sa.attention under torch.autograd returns the same O and the same
+    gradients, bit for bit, as the direct fwd / bwd calls."""
+    require_gpu()
+    import sparse_attention_sepattn_amd as sa
+    inp = _inputs(333, 2, 4, 2, 64, "bf16", 4, 64, 0.08, 11)
+    c = inp["cfg"]
+    q, k, v, do = (dev_tensor(inp[x], "bf16") for x in ("q", "k", "v", "do"))
+    idx = sa.build_index(torch.from_numpy(inp["tok"]).cuda(), inp["sep"], c["a"], c["n"])
+    o, lse = sa.fwd(q, k, v, idx, inp["scale"])
+    ref = sa.bwd(q, k, v, o, lse, do, idx, inp["scale"])
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    oa = sa.attention(qa, ka, va, idx, inp["scale"])
+    oa.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.detach(), o)
+    for name, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), ref):
+        assert torch.equal(got, want), name
