@@ -178,3 +178,16 @@ def test_decode_is_deterministic():
     o1 = cache.decode(q, cos, sin).clone()
     o2 = cache.decode(q, cos, sin).clone()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 64), (3, 3, 128), (4, 2, 128), (8, 2, 64), (4, 1, 64), (8, 1, 128)])
+def test_decode_every_group_size_and_head_dim(Hq, Hkv, d):
+    """Every built decode variant (query heads per kv head G = 1, 2, 4, 8 at
+    d = 64 and 128) against the oracle, with a cache long enough (c = 300) to
+    split over three 128-slot chunks before the first compression."""
+    require_gpu()
+    say(f"decode Hq={Hq} Hkv={Hkv} d={d}")
+    worst, nc = _stream_run(B=2, Hkv=Hkv, Hq=Hq, d=d, c=300, a=4, s=16, w=64, steps=700, p_sep=0.1,
+                            seed=Hq * 10 + Hkv + d, check_every=100, decode_every=37)
+    say(f"  compressions per sequence={nc} decode max err={worst:.3g}")
+    assert nc.min() >= 2 and worst <= 2e-2
