@@ -81,13 +81,13 @@ def sep_mask(tok, sep_ids, a, n):
     return mask_rows(sep, a, n, np.arange(S))
 
 
-def row_nnz(sep, a, n):
-    """Number of visible keys of every query row, counted from the mask."""
+def row_nnz(sep, a, n, row_block=1024):
+    """Number of visible keys of every query row, counted from the mask
+    (``mask_rows`` of ``row_block`` rows at a time, to bound memory)."""
     S = sep.shape[0]
     out = np.zeros(S, dtype=np.int64)
-    blk = 1024
-    for r0 in range(0, S, blk):
-        rows = np.arange(r0, min(S, r0 + blk))
+    for r0 in range(0, S, row_block):
+        rows = np.arange(r0, min(S, r0 + row_block))
         out[rows] = mask_rows(sep, a, n, rows).sum(axis=1)
     return out
 

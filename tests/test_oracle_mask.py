@@ -142,6 +142,60 @@ def test_streaming_reduction():
         assert np.array_equal(sepmask.sep_mask(tok, [7], a, n), band | sink)
 
 
+def _nnz_closed_form(sep, a, n):
+    """Visible keys of row i, from the partition of the row (atlas.scime.ai,
+    "Approach"): the whole window [lo_i, i] with lo_i = max(0, i - n + 1),
+    plus the initial tokens below lo_i and the separators in [a, lo_i).  The
+    separator counts are a running sum taken here, not the oracle's index."""
+    sep = np.asarray(sep, dtype=bool)
+    S = sep.shape[0]
+    j = np.arange(S)
+    cnt = np.concatenate([[0], np.cumsum(sep & (j >= a))])  # separators in [a, x)
+    i = np.arange(S)
+    lo = np.maximum(0, i - n + 1)
+    return (i - lo + 1) + np.minimum(a, lo) + cnt[lo]
+
+
+@pytest.mark.parametrize("S", [1, 3, 6, 8])
+def test_row_nnz_brute_force_all_patterns(S):
+    """row_nnz equals the row sums of the per-element brute-force mask and
+    the closed form, for every separator pattern, a and n, with row blocks
+    smaller than, equal to and larger than S."""
+    for flags in itertools.product([False, True], repeat=S):
+        sep = np.array(flags, dtype=bool)
+        for a in range(0, 4):
+            for n in range(1, S + 2):
+                want = _brute_mask(sep, a, n).sum(axis=1)
+                assert np.array_equal(want, _nnz_closed_form(sep, a, n))
+                for blk in (1, 3, S, S + 5):
+                    assert np.array_equal(sepmask.row_nnz(sep, a, n, row_block=blk), want), (flags, a, n, blk)
+
+
+def test_row_nnz_random_longer_blocked():
+    """Longer random sequences (up to 2600 keys, past the default block of
+    1024 rows) against the closed form, with blocks that leave a ragged last
+    block."""
+    r = np.random.default_rng(77)
+    for S, blk in [(2600, 1024), (1500, 1024), (700, 97), (129, 64), (64, 64), (300, 299)]:
+        sep = r.random(S) < r.random() * 0.3
+        a = int(r.integers(0, 8))
+        for n in (1, 2, 64, 255, S, S + 3):
+            assert np.array_equal(sepmask.row_nnz(sep, a, n, row_block=blk), _nnz_closed_form(sep, a, n)), (S, a, n)
+
+
+def test_row_nnz_special_cases():
+    """No separators and a = 0: min(i + 1, n) keys; every token a separator
+    or n >= S: i + 1 keys (causal); n = 1 and no separators: the query and
+    the initial tokens below it."""
+    S = 300
+    i = np.arange(S)
+    none = np.zeros(S, dtype=bool)
+    assert np.array_equal(sepmask.row_nnz(none, 0, 17, row_block=50), np.minimum(i + 1, 17))
+    assert np.array_equal(sepmask.row_nnz(np.ones(S, dtype=bool), 0, 1, row_block=64), i + 1)
+    assert np.array_equal(sepmask.row_nnz(none, 3, S, row_block=128), i + 1)
+    assert np.array_equal(sepmask.row_nnz(none, 4, 1, row_block=100), np.minimum(i, 4) + 1)
+
+
 def test_kept_entries_counts_tiles():
     tok = np.arange(300) % 13
     idx = sepmask.build_index(tok, [0, 5], 4, 64)

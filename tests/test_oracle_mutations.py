@@ -65,6 +65,34 @@ def test_mask_pins_catch_planted_mistakes(kind, monkeypatch, golden):
         assert failed, kind
 
 
+def _row_nnz(kind):
+    def row_nnz(sep, a, n, row_block=1024):
+        S = sep.shape[0]
+        out = np.zeros(S, dtype=np.int64)
+        for r0 in range(0, S, row_block):
+            hi = min(S, r0 + row_block)
+            if kind == "last_row_of_block_dropped":
+                hi = max(r0, hi - 1)
+            rows = np.arange(r0, hi)
+            if kind == "causal_count_only":
+                out[rows] = rows + 1
+            else:
+                out[rows] = sepmask.mask_rows(sep, a, n, rows).sum(axis=1)
+        return out
+    return row_nnz
+
+
+@pytest.mark.parametrize("kind", ["none", "last_row_of_block_dropped", "causal_count_only"])
+def test_row_nnz_pins_catch_planted_mistakes(kind, monkeypatch):
+    monkeypatch.setattr(sepmask, "row_nnz", _row_nnz(kind))
+    failed = _failures([(pm.test_row_nnz_brute_force_all_patterns, (6,)), (pm.test_row_nnz_random_longer_blocked, ()),
+                        (pm.test_row_nnz_special_cases, ())])
+    if kind == "none":
+        assert failed == []
+    else:
+        assert failed, kind
+
+
 # --- attention forward / backward ----------------------------------------------
 
 def _masked_softmax(kind):
@@ -191,6 +219,38 @@ def test_cache_update_pins_catch_planted_mistakes(kind, monkeypatch, golden):
     monkeypatch.setattr(sepcache.SepCacheSim, "append", _append(kind))
     failed = _failures([(pc.test_golden_trace, (golden,)), (pc.test_invariants, (2, 2, 3, 8, 0.4)),
                         (pc.test_cache_equals_mask_row_when_compressing_every_overflow, (2, 5, 0.3))])
+    if kind == "none":
+        assert failed == []
+    else:
+        assert failed, kind
+
+
+def _cache_arrays(kind):
+    def cache_arrays(sim, c, Hkv, d):
+        slots = sim.I + sim.W + sim.Sp if kind == "window_before_separators" else sim.slots()
+        L = len(slots)
+        k = np.zeros((Hkv, c, d), dtype=np.uint16)
+        v = np.zeros((Hkv, c, d), dtype=np.uint16)
+        fill = 0 if kind == "zero_past_length" else -1
+        pos = np.full(c, fill, dtype=np.int32)
+        tok = np.full(c, fill, dtype=np.int32)
+        for i, e in enumerate(slots):
+            k[:, i, :] = e.k
+            v[:, i, :] = e.k if kind == "value_from_key" else e.v
+            pos[i] = e.pos
+            tok[i] = e.tok
+        n_init, n_sep, n_win, t = sim.state()
+        if kind == "counters_swapped":
+            n_sep, n_win = n_win, n_sep
+        return k[:, :L], v[:, :L], pos, tok, np.array([n_init, n_sep, n_win, t], dtype=np.int32)
+    return cache_arrays
+
+
+@pytest.mark.parametrize("kind", ["none", "window_before_separators", "zero_past_length", "value_from_key",
+                                  "counters_swapped"])
+def test_cache_arrays_pins_catch_planted_mistakes(kind, monkeypatch, golden):
+    monkeypatch.setattr(sepcache, "cache_arrays", _cache_arrays(kind))
+    failed = _failures([(pc.test_cache_arrays_golden_trace, (golden,))])
     if kind == "none":
         assert failed == []
     else:

@@ -40,6 +40,40 @@ def test_golden_trace(golden):
     assert t == 14
 
 
+def _payload(pos, Hkv, d, salt):
+    """A bf16 bit pattern [Hkv, d] that names its stream position, head and
+    element (so a row placed in the wrong slot, head or element is seen)."""
+    h = np.arange(Hkv)[:, None]
+    j = np.arange(d)[None, :]
+    return ((pos * 977 + h * 131 + j * 7 + salt) % 65521).astype(np.uint16)
+
+
+def test_cache_arrays_golden_trace(golden):
+    """cache_arrays lays the cache out as slots I, Sp, W: after every step of
+    the hand-derived trace, slot i holds the payload, position and id of the
+    trace's i-th position, slots past L hold -1, and the counters are the
+    trace's (n_init, n_sep, n_win, tokens seen)."""
+    g = golden("sepcache_trace.txt")
+    a, s, w, c = (int(g[x]) for x in ("a", "s", "w", "c"))
+    seps = set(int(x) for x in g["separators_at"].split())
+    Hkv, d = 3, 5
+    sim = sepcache.SepCacheSim(a, s, w, c, sep_ids=[1])
+    for t in range(14):
+        tok = 1 if t in seps else 20 + t
+        sim.append(tok, _payload(t, Hkv, d, 0), _payload(t, Hkv, d, 11))
+        want = [int(x) for x in g[f"t{t}"].split() if x != "C"]
+        L = len(want)
+        k, v, pos, tk, st = sepcache.cache_arrays(sim, c, Hkv, d)
+        assert k.shape == (Hkv, L, d) and v.shape == (Hkv, L, d), t
+        for i, p in enumerate(want):
+            assert np.array_equal(k[:, i, :], _payload(p, Hkv, d, 0)), (t, i)
+            assert np.array_equal(v[:, i, :], _payload(p, Hkv, d, 11)), (t, i)
+        assert list(pos) == want + [-1] * (c - L), t
+        assert list(tk) == [1 if p in seps else 20 + p for p in want] + [-1] * (c - L), t
+        assert list(st) == [int(x) for x in g[f"state{t}"].split()], t
+        assert pos.dtype == np.int32 and tk.dtype == np.int32 and st.dtype == np.int32
+
+
 def _stream(r, steps, p):
     return np.where(r.random(steps) < p, 1, 2)
 
