@@ -103,6 +103,41 @@ class Events:
         self.made = []
 
 
+class EventRing:
+    """Times many intervals with a fixed set of events: groups of `width`
+    events are handed out until `depth` groups are in use, then the stream is
+    synchronised, the recorded groups are read (the times of consecutive
+    events of each group) and the groups are reused.  The number of live
+    events stays at depth * width however many steps a pass runs (a pass of
+    4096 steps with a new event pair per step kept ~13 000 events alive at
+    once, and the process died under the counter profiler)."""
+
+    def __init__(self, ev, width, depth=256):
+        self.ev, self.width = ev, width
+        self.groups = [ev.new(width) for _ in range(depth)]
+        self.used = 0
+        self.times = []  # per group: width - 1 intervals (ms)
+
+    def take(self):
+        if self.used == len(self.groups):
+            self.harvest()
+        g = self.groups[self.used]
+        self.used += 1
+        return g
+
+    def harvest(self):
+        import torch
+        torch.cuda.synchronize()
+        for g in self.groups[:self.used]:
+            self.times.append([self.ev.ms(g[i], g[i + 1]) if g[i] and g[i + 1] else None
+                               for i in range(self.width - 1)])
+        self.used = 0
+
+    def result(self):
+        self.harvest()
+        return self.times
+
+
 def schedule_counts(qtile, sep_prefix, a, n, S, tk=64):
     """Kept-tile entries (total, anchor part, band part) and visible entries
     of one sequence, from its index (qtile fields and separator prefix)."""
@@ -115,6 +150,11 @@ def schedule_counts(qtile, sep_prefix, a, n, S, tk=64):
     lo = np.maximum(0, i - n + 1)
     nnz = int(((i - lo + 1) + np.minimum(a, lo) + sep_prefix.astype(np.int64)[lo]).sum())
     return E, Ea, Eb, nnz
+
+
+TRAFFIC_SOURCE = ("profiles/traffic.json: FETCH_SIZE and WRITE_SIZE from two rocprofv3 --pmc runs of this bench, "
+                  "scaled by a known-size copy; not measured in this run (reported only while the kernel's "
+                  "source hash matches)")
 
 
 def traffic_from_profiles(kernel):
@@ -268,7 +308,7 @@ def prefill_leg(args, torch, sa, synth):
                     useful_gflop_fwd_bwd=round(14 * d * nnz / 1e9, 3), tile_efficiency=round(nnz / E, 4),
                     wall_ms_per_step=round(wall / K * 1e3, 4)),
         kernels_ms_untimed_pass={nm: round(x, 5) for nm, x in avg.items()},
-        roofline=dict(kernel=kernel_symbol, **binding, traffic=traffic,
+        roofline=dict(kernel=kernel_symbol, **binding, traffic=traffic, traffic_source=TRAFFIC_SOURCE if traffic else None,
                       algorithmic_mb_per_launch=round(kernel_bytes[dominant] / 1e6, 3),
                       algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
                       executed_gflop_per_launch=round(executed_flops[dominant] / 1e9, 3),
@@ -449,30 +489,38 @@ def decode_leg(args, torch, sa, synth):
     # per-kernel breakdown (events between every kernel); not the timed region
     cache.init()
     nb = min(T, args.decode_breakdown_steps)
-    marks = [ev.new(4) for _ in range(nb)]
+    ring = EventRing(ev, 4)
     for t in range(nb):
-        m = marks[t]
+        m = ring.take()
         ev.record(m[0], stream)
         cache.update(ks[t], vs[t], toks[t], sep)
         cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=m[1:4])
-    torch.cuda.synchronize()
+    bt = ring.result()
     lob = nb // 2
-    upd = np.array([ev.ms(m[0], m[1]) for m in marks][lob:])
-    mrg = np.array([ev.ms(m[2], m[3]) for m in marks][lob:])
+    upd = np.array([x[0] for x in bt][lob:])
+    mrg = np.array([x[2] for x in bt][lob:])
 
-    # timed region: T update + decode steps; events only around the decode kernel
+    # timed region: T update + decode steps, events only at its ends
     cache.init()
-    marks = [ev.new(2) for _ in range(T)]
     t0, t1 = ev.new(2)
     torch.cuda.synchronize()
     ev.record(t0, stream)
     for t in range(T):
         cache.update(ks[t], vs[t], toks[t], sep)
-        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[marks[t][0], marks[t][1], None])
+        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws)
     ev.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = ev.ms(t0, t1)
-    dec = np.array([ev.ms(m[0], m[1]) for m in marks])
+
+    # the decode kernel alone, cache-warm: the same steps with an event pair
+    # around every decode kernel (read back in groups, outside the kernels)
+    cache.init()
+    ring = EventRing(ev, 2)
+    for t in range(T):
+        cache.update(ks[t], vs[t], toks[t], sep)
+        m = ring.take()
+        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[m[0], m[1], None])
+    dec = np.array([x[0] for x in ring.result()])
 
     # flushed pass: at every 8th step of the steady state, reading 512 MB of
     # scratch evicts the K/V working set (at most ~210 MB here, below the
@@ -486,17 +534,18 @@ def decode_leg(args, torch, sa, synth):
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     cache.init()
     sampled = [t for t in range(lo, T) if (t - lo) % flush_every == 0]
-    fmarks = {t: ev.new(2) for t in sampled}
+    sampled_set = set(sampled)
+    ring = EventRing(ev, 2, depth=64)
     torch.cuda.synchronize()
     for t in range(T):
         cache.update(ks[t], vs[t], toks[t], sep)
-        if t in fmarks:
+        if t in sampled_set:
             torch.sum(scratch, dim=(0,), out=flush_sink)
-            cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[fmarks[t][0], fmarks[t][1], None])
+            m = ring.take()
+            cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[m[0], m[1], None])
         else:
             cache.decode(qs[t], cos, sin, scale, o=out, ws=ws)
-    torch.cuda.synchronize()
-    fdec = np.array([ev.ms(fmarks[t][0], fmarks[t][1]) for t in sampled])
+    fdec = np.array([x[0] for x in ring.result()])
     del scratch, flush_sink
     ev.close()
     handoff = prefill_handoff(torch, sa, synth, cfg, sep, cos.device)
@@ -526,6 +575,7 @@ def decode_leg(args, torch, sa, synth):
         step_GBps=round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
         roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(float(gbs), 1), peak=PEAK_HBM_GBS,
                       unit="GB/s", frac=round(float(gbs) / PEAK_HBM_GBS, 4), traffic=traffic,
+                      traffic_source=TRAFFIC_SOURCE if traffic else None,
                       algorithmic_MB_per_launch=round(float(dec_bytes[sampled].mean()) / 1e6, 3)),
     )
 
@@ -591,6 +641,7 @@ def cpu_leg(args, inp, E_seqs):
                sample=f"fp64 numpy oracle fwd+bwd of sequences 0..{nb - 1}, all {Hq} heads, of the same inputs "
                       f"({nb * Hq} of {cfg['B'] * Hq} (sequence, head) pairs), {spent:.1f} s",
                seconds=round(spent, 2))
+    out["cpu_model"] = cpu_model()
     try:  # the same oracle on one thread, sequence 0
         from threadpoolctl import threadpool_limits
         sl = (slice(0, 1), slice(0, Hq))
@@ -603,9 +654,41 @@ def cpu_leg(args, inp, E_seqs):
             t1 = time.perf_counter() - t
         out["single_thread"] = dict(value=round((4 + 10) * d * E_seqs[0] * Hq / t1 / 1e12, 6), unit="TFLOP/s",
                                     cores=1, sample=f"sequence 0, all {Hq} heads, {t1:.1f} s")
+        out["tiny_fp32_forward_single_thread"] = tiny_oracle_time(threadpool_limits)
     except ImportError:
         pass
     return out
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it, from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def tiny_oracle_time(threadpool_limits, reps=5):
+    """The fp32 parity configuration (B1 H1 S512 d64, forward) through the
+    oracle on one thread: median wall time of `reps` runs."""
+    import synth
+    from oracle import attention
+    cfg = synth.CONFIGS["tiny_fp32"]
+    inp = synth.prefill_inputs(cfg)
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t = time.perf_counter()
+            attention.attention_forward(inp["qf"], inp["kf"], inp["vf"], inp["tok"], inp["sep"], cfg["a"], cfg["n"],
+                                        scale=inp["scale"])
+            times.append(time.perf_counter() - t)
+    return dict(ms=round(float(np.median(times)) * 1e3, 3), cores=1,
+                sample=f"B1 H1 S512 d64 fp32 forward, median of {reps} runs")
 
 
 def main():

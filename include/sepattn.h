@@ -56,8 +56,13 @@ extern "C" {
 #define SEPATTN_EUNSUPPORTED 2 /* dtype / head-dim combination not built (d must be 64 or 128); one
                                   (sequence, head) slice S*d*element size at or above 2^31 bytes;
                                   more than 65535 query tiles of 128 rows, batch entries, or
-                                  batch x kv-head pairs (launch grid dimensions) */
-#define SEPATTN_ECAPACITY 3    /* SepCache capacities: need w >= 1, s >= 0, a >= 0 and c > a + s + w */
+                                  batch x kv-head pairs (launch grid dimensions); a SepCache with
+                                  more than 128 kv heads (Hkv <= 128: one slot of every head, K and
+                                  V, must fit the update kernel's 128 KB move chunk); a decode
+                                  group Hq / Hkv that is not 1, 2, 4 or 8 */
+#define SEPATTN_ECAPACITY 3    /* SepCache capacities: need w >= 1, s >= 0, a >= 0, c > a + s + w,
+                                  and c <= 8192 (the update kernel plans a compression of the c
+                                  slots in LDS) */
 #define SEPATTN_EWORKSPACE 4   /* workspace smaller than the matching *_workspace() query */
 #define SEPATTN_EHIP 5         /* a HIP launch failed */
 
@@ -149,7 +154,9 @@ int sepattn_build_index_interval(int B, int S, int interval, int a, int n, sepat
 /* Forward.  q [B,Hq,S,d], k/v [B,Hkv,S,d] of `dtype`, scale > 0 (e.g. 1/sqrt(d)),
  * idx built for these B, S.  Writes o [B,Hq,S,d] (dtype) and lse [B,Hq,S]
  * fp32 = natural log of each row's softmax normaliser of the scaled scores.
- * Supported: dtype F32 or BF16 with d in {64, 128}.  No workspace. */
+ * Supported: dtype F32 or BF16 with d in {64, 128}.  Takes no workspace (and
+ * so has no size query): every query tile's running statistics live in
+ * registers and its K/V tiles in LDS. */
 int sepattn_fwd(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int S, int d,
                 int dtype, float scale, const sepattn_index* idx, void* o, float* lse, void* stream);
 
@@ -209,7 +216,9 @@ typedef struct {
 int sepcache_init(const sepcache* cache, void* stream);
 
 /* Append one token per sequence: k_new/v_new [B, Hkv, d] bf16 (no rotary
- * embedding), tok_new [B] int32.  The token joins the Initial block while it
+ * embedding), tok_new [B] int32.  Takes no workspace (and so has no size
+ * query): a compression's move plan lives in the LDS of one workgroup per
+ * sequence.  The token joins the Initial block while it
  * holds fewer than a tokens, else the Window; if usage then equals c, the
  * Past Window (all but the w newest Window tokens) is compressed: its
  * separators (ids in `sep_ids`, HOST array of n_sep int32) join the Separator
@@ -233,14 +242,20 @@ int sepcache_update(const sepcache* cache, const void* k_new, const void* v_new,
 int sepcache_prefill(const sepcache* cache, const void* k, const void* v, const int32_t* tok, int P,
                      const sepattn_index* idx, void* stream);
 
-/* Device workspace bytes sepcache_decode needs for Hq query heads. */
+/* Device workspace bytes sepcache_decode needs for Hq query heads (the
+ * size depends on Hq as well as on the cache: one fp32 partial per query
+ * head and 128-slot chunk).  0 if the cache or Hq is invalid. */
 size_t sepcache_decode_workspace(const sepcache* cache, int Hq);
 
 /* Decode attention of the newest token of every sequence over its cache:
- * q [B, Hq, d] bf16 (no rotary embedding; Hq a multiple of Hkv) is rotated at
- * slot L-1, the key in slot k at slot k, using rope_cos/rope_sin [c, d/2] fp32
- * (see sepattn_rope_table_host); o [B, Hq, d] bf16 = softmax(scale q.K^T) V
- * over the L slots.  `ws`: >= sepcache_decode_workspace() bytes. */
+ * q [B, Hq, d] bf16 (no rotary embedding; Hq a multiple of Hkv with
+ * Hq / Hkv in {1, 2, 4, 8}) is rotated at slot L-1, the key in slot k at
+ * slot k, using rope_cos/rope_sin [c, d/2] fp32 (see
+ * sepattn_rope_table_host); o [B, Hq, d] bf16 = softmax(scale q.K^T) V over
+ * the L slots.  A sequence whose cache is empty (L = 0: nothing appended
+ * since sepcache_init) gets o = 0.  `ws`: device scratch of >=
+ * sepcache_decode_workspace() bytes, 256-byte aligned; its contents on entry
+ * do not matter.  EWORKSPACE if ws_bytes is smaller. */
 int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
                     const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                     void* stream);

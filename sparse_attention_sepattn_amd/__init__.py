@@ -139,9 +139,11 @@ def _host_ids(sep_ids):
     return arr, arr.ctypes.data_as(ctypes.c_void_p)
 
 
-def _need(t, name, dtype=None, shape=None):
+def _need(t, name, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -213,16 +215,16 @@ def fwd(q, k, v, index, scale=None, o=None, lse=None):
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     _need(q, "q")
-    _need(k, "k", q.dtype, (B, Hkv, S, d))
-    _need(v, "v", q.dtype, (B, Hkv, S, d))
+    _need(k, "k", q.dtype, (B, Hkv, S, d), q.device)
+    _need(v, "v", q.dtype, (B, Hkv, S, d), q.device)
     if scale is None:
         scale = d ** -0.5
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    _need(o, "o", q.dtype, q.shape)
-    _need(lse, "lse", torch.float32, (B, Hq, S))
+    _need(o, "o", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, S), q.device)
     _check(load_library().sepattn_fwd(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, S, d, _dtype_code(q),
                                       float(scale), ctypes.byref(index.st), _ptr(o), _ptr(lse),
                                       _stream()), "fwd")
@@ -240,20 +242,25 @@ def bwd(q, k, v, o, lse, dout, index, scale=None, dq=None, dk=None, dv=None, ws=
     kernels (see sepattn_bwd_profiled)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
+    dev = q.device
     for t, name in ((q, "q"), (o, "o"), (dout, "dout")):
-        _need(t, name, q.dtype, q.shape)
-    _need(k, "k", q.dtype, (B, Hkv, S, d))
-    _need(v, "v", q.dtype, (B, Hkv, S, d))
-    _need(lse, "lse", torch.float32, (B, Hq, S))
+        _need(t, name, q.dtype, q.shape, dev)
+    _need(k, "k", q.dtype, (B, Hkv, S, d), dev)
+    _need(v, "v", q.dtype, (B, Hkv, S, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, S), dev)
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, q.shape, dev)
+    _need(dk, "dk", q.dtype, k.shape, dev)
+    _need(dv, "dv", q.dtype, v.shape, dev)
     L = load_library()
     nbytes = L.sepattn_bwd_workspace(B, Hq, Hkv, S, d, _dtype_code(q))
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", torch.uint8, None, dev)  # its size is checked by the library (EWORKSPACE)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), B, Hq, Hkv, S, d, _dtype_code(q),
             float(scale), ctypes.byref(index.st), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream())
     if events is None:
@@ -322,9 +329,10 @@ class SepCache:
         _check(load_library().sepcache_init(ctypes.byref(self.st), _stream()), "sepcache_init")
 
     def update(self, k_new, v_new, tok_new, sep_ids):
-        _need(k_new, "k_new", torch.bfloat16, (self.B, self.Hkv, self.d))
-        _need(v_new, "v_new", torch.bfloat16, (self.B, self.Hkv, self.d))
-        _need(tok_new, "tok_new", torch.int32, (self.B,))
+        dev = self.k.device
+        _need(k_new, "k_new", torch.bfloat16, (self.B, self.Hkv, self.d), dev)
+        _need(v_new, "v_new", torch.bfloat16, (self.B, self.Hkv, self.d), dev)
+        _need(tok_new, "tok_new", torch.int32, (self.B,), dev)
         ids, ids_p = _host_ids(sep_ids)
         _check(load_library().sepcache_update(ctypes.byref(self.st), _ptr(k_new), _ptr(v_new), _ptr(tok_new),
                                               ids_p, len(ids), _stream()), "sepcache_update")
@@ -333,10 +341,11 @@ class SepCache:
         """Set the caches to what streaming the prompt ``tok`` [B,P] (rows
         k/v [B,Hkv,P,d] bf16) through ``update`` would leave; ``index`` is
         build_index(tok, sep_ids, a, n) with this cache's ``a``."""
-        _need(tok, "tok", torch.int32)
+        dev = self.k.device
+        _need(tok, "tok", torch.int32, None, dev)
         B, P = tok.shape
-        _need(k, "k", torch.bfloat16, (self.B, self.Hkv, P, self.d))
-        _need(v, "v", torch.bfloat16, (self.B, self.Hkv, P, self.d))
+        _need(k, "k", torch.bfloat16, (self.B, self.Hkv, P, self.d), dev)
+        _need(v, "v", torch.bfloat16, (self.B, self.Hkv, P, self.d), dev)
         _check(load_library().sepcache_prefill(ctypes.byref(self.st), _ptr(k), _ptr(v), _ptr(tok), P,
                                                ctypes.byref(index.st), _stream()), "sepcache_prefill")
 
@@ -347,19 +356,22 @@ class SepCache:
         """Decode attention of the newest token; ``events``: optional 3
         hipEvent_t handles recorded around the two kernels."""
         B, Hq, d = q.shape
-        _need(q, "q", torch.bfloat16, (self.B, Hq, self.d))
-        _need(rope_cos, "rope_cos", torch.float32, (self.c, self.d // 2))
-        _need(rope_sin, "rope_sin", torch.float32, (self.c, self.d // 2))
+        dev = self.k.device
+        _need(q, "q", torch.bfloat16, (self.B, Hq, self.d), dev)
+        _need(rope_cos, "rope_cos", torch.float32, (self.c, self.d // 2), dev)
+        _need(rope_sin, "rope_sin", torch.float32, (self.c, self.d // 2), dev)
         if scale is None:
             scale = d ** -0.5
         if o is None:
             o = torch.empty_like(q)
+        _need(o, "o", torch.bfloat16, (self.B, Hq, self.d), dev)
         L = load_library()
         nbytes = L.sepcache_decode_workspace(ctypes.byref(self.st), Hq)
         if ws is None:
             if self._ws is None or self._ws.numel() < nbytes:
-                self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+                self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
             ws = self._ws
+        _need(ws, "ws", torch.uint8, None, dev)  # its size is checked by the library (EWORKSPACE)
         args = (ctypes.byref(self.st), _ptr(q), Hq, _ptr(rope_cos), _ptr(rope_sin), float(scale), _ptr(o),
                 _ptr(ws), ws.numel(), _stream())
         if events is None:

@@ -64,8 +64,12 @@ const char* sepattn_strerror(int status) {
   switch (status) {
     case SEPATTN_OK: return "ok";
     case SEPATTN_EINVAL: return "invalid argument";
-    case SEPATTN_EUNSUPPORTED: return "unsupported dtype or head dimension";
-    case SEPATTN_ECAPACITY: return "invalid SepCache capacities (need w >= 1 and c > a + s + w)";
+    case SEPATTN_EUNSUPPORTED:
+      return "unsupported shape: dtype or head dimension (d must be 64 or 128), a slice of 2^31 bytes or more, "
+             "a launch grid dimension above 65535, more than 128 SepCache kv heads, or a decode group "
+             "Hq/Hkv other than 1, 2, 4, 8";
+    case SEPATTN_ECAPACITY:
+      return "invalid SepCache capacities (need a >= 0, s >= 0, w >= 1, c > a + s + w and c <= 8192)";
     case SEPATTN_EWORKSPACE: return "workspace too small";
     case SEPATTN_EHIP: return "HIP launch failed";
     default: return "unknown status";

@@ -359,7 +359,8 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(DecArgs p) {
     }
     M = Mn;
   }
-  p.o[(size_t)bh * D + dd] = f32_to_bf16_bits(num / den);
+  // an empty cache (L = 0) has no chunk: its output is zero
+  p.o[(size_t)bh * D + dd] = f32_to_bf16_bits(den > 0.f ? num / den : 0.f);
 }
 
 static int n_splits(int c) { return (c - 1 + kDecChunk - 1) / kDecChunk; }

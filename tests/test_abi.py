@@ -130,6 +130,39 @@ def test_cache_capacity_errors():
     assert L.sepcache_decode(ctypes.byref(c), fp, 96, fp, fp, 0.1, fp, fp, 1 << 30, z) == 2  # group of 12
 
 
+def test_cache_hard_limits():
+    """The hard limits stated in sepattn.h: capacity c <= 8192 (ECAPACITY),
+    at most 128 kv heads (EUNSUPPORTED), a decode group Hq/Hkv of 1, 2, 4 or
+    8 (EUNSUPPORTED), decode workspace size and alignment (EWORKSPACE,
+    EINVAL) -- all on the host, before any launch."""
+    L = sa.load_library()
+    fake = 1 << 40
+    fp = ctypes.c_void_p(fake)
+    z = ctypes.c_void_p(0)
+    c = sa._Cache(2, 8, 128, 8192, 4, 64, 256, fake, fake, fake, fake, fake)
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 32) > 0       # c = 8192 is accepted
+    c.c = 8193
+    assert L.sepcache_init(ctypes.byref(c), z) == 3
+    assert L.sepcache_update(ctypes.byref(c), fp, fp, fp, None, 0, z) == 3
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 32) == 0
+    c.c, c.Hkv = 800, 128
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 128) > 0      # Hkv = 128 is accepted
+    c.Hkv = 129
+    assert L.sepcache_init(ctypes.byref(c), z) == 2
+    assert L.sepcache_update(ctypes.byref(c), fp, fp, fp, None, 0, z) == 2
+    c.Hkv = 8
+    need = L.sepcache_decode_workspace(ctypes.byref(c), 32)
+    for Hq in (24, 48, 128):  # groups of 3, 6 and 16
+        assert L.sepcache_decode(ctypes.byref(c), fp, Hq, fp, fp, 0.1, fp, fp, 1 << 30, z) == 2, Hq
+    assert L.sepcache_decode(ctypes.byref(c), fp, 32, fp, fp, 0.1, fp, fp, need - 1, z) == 4
+    assert L.sepcache_decode(ctypes.byref(c), ctypes.c_void_p(fake + 16), 32, fp, fp, 0.1, fp,
+                             ctypes.c_void_p(fake + 16), need, z) == 1      # ws not 256-byte aligned
+    assert L.sepcache_decode(ctypes.byref(c), fp, 32, fp, fp, 0.0, fp, fp, need, z) == 1   # scale <= 0
+    for st in (2, 3):
+        text = L.sepattn_strerror(st).decode()
+        assert ("128" in text) if st == 2 else ("8192" in text), text
+
+
 def test_rope_table_host_matches_double_precision():
     c, d, theta = 800, 128, 500000.0
     cos, sin = sa.rope_table(theta, c, d)

@@ -125,14 +125,25 @@ def test_bwd_pythia_config_full():
     _check(got, ref, "bf16", "pythia")
 
 
+_LONG = {}
+
+
+def _long_context():
+    """Inputs and GPU gradients of the 32k-token configuration, computed once
+    for the tests that sample them."""
+    if not _LONG:
+        cfg = synth.CONFIGS["long_context_32k"]
+        inp = synth.prefill_inputs(cfg)
+        _LONG.update(cfg=cfg, inp=inp, grads=_gpu_grads(inp))
+    return _LONG["cfg"], _LONG["inp"], _LONG["grads"]
+
+
 def test_bwd_long_context_sampled():
     """32k tokens, 32 q / 8 kv heads, bursty separators: dQ on sampled rows of
     heads 0 and 31; dK/dV on sampled key rows of the last 2048 positions of kv
     heads 0 and 7 (each needs every query row's softmax statistics)."""
     require_gpu()
-    cfg = synth.CONFIGS["long_context_32k"]
-    inp = synth.prefill_inputs(cfg)
-    dq, dk, dv = _gpu_grads(inp)
+    cfg, inp, (dq, dk, dv) = _long_context()
     S, grp = cfg["S"], cfg["Hq"] // cfg["Hkv"]
     sepf = sepmask.separator_flags(inp["tok"][0], inp["sep"])
     rows = np.unique(np.concatenate([np.arange(0, S, 331), np.arange(S - 70, S), np.arange(0, 70)]))
@@ -153,6 +164,32 @@ def test_bwd_long_context_sampled():
             rmax, rfro = _rel(got, ref)
             say(f"  32k {name} kv head {g}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
             assert rmax <= 3e-2 and rfro <= 1e-2
+
+
+def test_bwd_long_context_early_anchors():
+    """32k tokens: dK/dV of kv head 0 on the initial tokens, the first 40
+    separators and every 997th key of the whole sequence.  The early anchors
+    collect gradient from every later query row; the backward splits that
+    sum over anchor chunks of query tiles and a band slot and adds them in
+    its last kernel, so these rows pin the multi-chunk path at full size
+    (one kv head keeps the fp64 cost bounded)."""
+    require_gpu()
+    cfg, inp, (dq, dk, dv) = _long_context()
+    S, grp = cfg["S"], cfg["Hq"] // cfg["Hkv"]
+    sepf = sepmask.separator_flags(inp["tok"][0], inp["sep"])
+    seps = np.nonzero(sepf)[0]
+    cols = np.unique(np.concatenate([np.arange(0, 70), seps[:40], np.arange(0, S, 997)]))
+    g = 0
+    hs = range(g * grp, (g + 1) * grp)
+    say(f"  32k early anchors: {len(cols)} key rows of kv head {g}")
+    rk, rv = attention.grad_kv_cols([inp["qf"][0, h] for h in hs], inp["kf"][0, g], inp["vf"][0, g],
+                                    [inp["dof"][0, h] for h in hs], sepf, cfg["a"], cfg["n"],
+                                    inp["scale"], cols)
+    for name, got, ref in (("dk", dk[0, g, cols], rk), ("dv", dv[0, g, cols], rv)):
+        rmax, rfro = _rel(got, ref)
+        say(f"  32k early {name} kv head {g}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+        assert rmax <= 3e-2 and rfro <= 1e-2
+    _LONG.clear()  # the last test that samples them
 
 
 def test_bwd_llama_config_sampled():

@@ -1,6 +1,8 @@
 """Streaming soak of the SepCache: a long update stream per sequence with the
-cache invariants checked on the GPU's own arrays every 1000 steps and full
-bit-exact parity with the oracle's list simulation at every check.
+cache invariants checked on the GPU's own arrays every 1000 steps, full
+bit-exact parity with the oracle's list simulation at every check, and at
+every check a decode of the newest token over the shifted cache compared with
+the oracle's decode attention over the simulated slots (max abs 2e-2).
 
 Invariants (all from pos/tok/state): length <= c - 1; the Initial block holds
 positions 0..min(t, a)-1; the Separator block holds at most s separators;
@@ -45,10 +47,15 @@ def test_streaming_soak():
     require_gpu()
     import sparse_attention_sepattn_amd as sa
     steps = int(os.environ.get("SEPATTN_SOAK_STEPS", "200000"))
-    B, Hkv, d, c, a, s, w = 2, 2, 64, 48, 4, 8, 16
+    B, Hkv, Hq, d, c, a, s, w = 2, 2, 4, 64, 48, 4, 8, 16
+    theta, scale = 500000.0, d ** -0.5
     r = synth.rng(77)
+    rq = synth.rng(78)  # the decode queries: a stream of their own
     sep = synth.separator_ids(r, 5000)
     cache = sa.SepCache(B, Hkv, d, c, a, s, w)
+    cos, sin = sa.rope_table(theta, c, d)
+    cos_d, sin_d = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    worst = 0.0
     sims = [osc.SepCacheSim(a, s, w, c, sep) for _ in range(B)]
     toks = np.zeros((steps, B), dtype=np.int32)
     chunk = 1000
@@ -68,6 +75,16 @@ def test_streaming_soak():
                 comps += int(sims[b].append(tok[i, b], kb[i, b], vb[i, b]))
         _invariants(cache, sep, a, s, w, c, t0 + n, toks)
         _compare_cache(cache, sims, Hkv, d, c, where=f"t={t0 + n}")
+        qb, qf = synth.normal(rq, (B, Hq, d), "bf16")
+        o = cache.decode(dev_tensor(qb, "bf16"), cos_d, sin_d, scale).float().cpu().numpy()
+        for b in range(B):
+            slots = sims[b].slots()
+            K = np.stack([synth.bf16_to_f64(e.k) for e in slots])  # [L, Hkv, d]
+            V = np.stack([synth.bf16_to_f64(e.v) for e in slots])
+            ref = osc.decode_attention(qf[b], K, V, scale, theta)
+            err = float(np.abs(o[b] - ref).max())
+            worst = max(worst, err)
+            assert err <= 2e-2, (t0 + n, b, err)
         if (t0 // chunk) % 50 == 0:
-            say(f"  t={t0 + n} compressions so far={comps}")
+            say(f"  t={t0 + n} compressions so far={comps} decode max err={worst:.3g}")
     assert comps > steps // 40
