@@ -30,7 +30,8 @@
  *
  * Conventions (every entry point):
  *   * Pointers are DEVICE pointers unless marked "host".  The caller owns all
- *     memory; the library never allocates or frees, keeps no global state and
+ *     memory; the library never allocates or frees, keeps no global state
+ *     (apart from the fixed decode scratch of sepcache_decode_noalloc) and
  *     may be called from several host threads on different streams.
  *   * `stream` is a hipStream_t passed as void*; all device work is enqueued
  *     on it and nothing synchronises the host.
@@ -65,6 +66,8 @@ extern "C" {
                                   slots in LDS) */
 #define SEPATTN_EWORKSPACE 4   /* workspace smaller than the matching *_workspace() query */
 #define SEPATTN_EHIP 5         /* a HIP launch failed */
+#define SEPATTN_ESCRATCH 6     /* sepcache_decode_noalloc: the input needs more than the library's
+                                  fixed scratch of SEPATTN_NOALLOC_SCRATCH_BYTES */
 
 /* element types of Q/K/V/O and gradients */
 #define SEPATTN_F32 0
@@ -259,6 +262,27 @@ size_t sepcache_decode_workspace(const sepcache* cache, int Hq);
 int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
                     const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* Size of the device scratch the library keeps for sepcache_decode_noalloc
+ * (per GPU, until the process ends). */
+#define SEPATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* sepcache_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus ws / ws_bytes),
+ * results and errors as sepcache_decode, computed by the same kernels; the
+ * chunk partials go to a fixed array of SEPATTN_NOALLOC_SCRATCH_BYTES in
+ * device memory that the library holds on every GPU it runs on until the
+ * process ends (its address is looked up on the first call on each device,
+ * with `stream`'s device current).  Nothing is allocated or freed by the
+ * call.  Limit: sepcache_decode_workspace(cache, Hq) must not exceed that
+ * size (16 MiB: e.g. B = 64, Hq = 32, c = 800, d = 128 needs 7.5 MiB), else
+ * ESCRATCH before any launch.  The array is shared by every call on one GPU
+ * and keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from several host threads) race and must be
+ * serialised by the caller. */
+int sepcache_decode_noalloc(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                            const float* rope_sin, float scale, void* o, void* stream);
 
 /* sepcache_decode with per-kernel timing: `events` is a HOST array of
  * n_events >= 3 hipEvent_t (as void*), recorded on `stream` before the decode

@@ -58,7 +58,7 @@ EXPORTS = ["sepattn_strerror", "sepattn_index_bytes", "sepattn_index_bind", "sep
            "sepattn_build_index_interval",
            "sepattn_fwd", "sepattn_bwd_workspace", "sepattn_bwd", "sepattn_bwd_profiled",
            "sepcache_init", "sepcache_update", "sepcache_prefill",
-           "sepcache_decode_workspace", "sepcache_decode", "sepcache_decode_profiled",
+           "sepcache_decode_workspace", "sepcache_decode", "sepcache_decode_noalloc", "sepcache_decode_profiled",
            "sepattn_rope_table_host"]
 
 
@@ -104,6 +104,8 @@ def load_library(path=None):
     L.sepcache_decode_workspace.argtypes = [ctypes.POINTER(_Cache), i32]
     L.sepcache_decode.restype = i32
     L.sepcache_decode.argtypes = [ctypes.POINTER(_Cache), vp, i32, vp, vp, f32, vp, vp, sz, vp]
+    L.sepcache_decode_noalloc.restype = i32
+    L.sepcache_decode_noalloc.argtypes = [ctypes.POINTER(_Cache), vp, i32, vp, vp, f32, vp, vp]
     L.sepcache_decode_profiled.restype = i32
     L.sepcache_decode_profiled.argtypes = [ctypes.POINTER(_Cache), vp, i32, vp, vp, f32, vp, vp, sz, vp, vp, i32]
     L.sepattn_rope_table_host.restype = i32
@@ -379,4 +381,23 @@ class SepCache:
         else:
             arr = (ctypes.c_void_p * len(events))(*events)
             _check(L.sepcache_decode_profiled(*args, arr, len(events)), "sepcache_decode_profiled")
+        return o
+
+    def decode_noalloc(self, q, rope_cos, rope_sin, scale=None, o=None):
+        """``decode`` through sepcache_decode_noalloc: no workspace, the
+        library's fixed per-device scratch holds the partials (calls that
+        overlap on one GPU race)."""
+        B, Hq, d = q.shape
+        dev = self.k.device
+        _need(q, "q", torch.bfloat16, (self.B, Hq, self.d), dev)
+        _need(rope_cos, "rope_cos", torch.float32, (self.c, self.d // 2), dev)
+        _need(rope_sin, "rope_sin", torch.float32, (self.c, self.d // 2), dev)
+        if scale is None:
+            scale = d ** -0.5
+        if o is None:
+            o = torch.empty_like(q)
+        _need(o, "o", torch.bfloat16, (self.B, Hq, self.d), dev)
+        _check(load_library().sepcache_decode_noalloc(ctypes.byref(self.st), _ptr(q), Hq, _ptr(rope_cos),
+                                                      _ptr(rope_sin), float(scale), _ptr(o), _stream()),
+               "sepcache_decode_noalloc")
         return o

@@ -72,6 +72,8 @@ const char* sepattn_strerror(int status) {
       return "invalid SepCache capacities (need a >= 0, s >= 0, w >= 1, c > a + s + w and c <= 8192)";
     case SEPATTN_EWORKSPACE: return "workspace too small";
     case SEPATTN_EHIP: return "HIP launch failed";
+    case SEPATTN_ESCRATCH:
+      return "input needs more than the library's fixed 16 MiB decode scratch (use sepcache_decode with a workspace)";
     default: return "unknown status";
   }
 }
@@ -245,6 +247,19 @@ int sepcache_decode(const sepcache* cache, const void* q, int Hq, const float* r
                     const float* rope_sin, float scale, void* o, void* ws, size_t ws_bytes,
                     void* stream) {
   return decode_common(cache, q, Hq, rope_cos, rope_sin, scale, o, ws, ws_bytes, stream, nullptr);
+}
+
+int sepcache_decode_noalloc(const sepcache* cache, const void* q, int Hq, const float* rope_cos,
+                            const float* rope_sin, float scale, void* o, void* stream) {
+  int st = check_cache(cache);
+  if (st != SEPATTN_OK) return st;
+  if (!q || !rope_cos || !rope_sin || !o || Hq < 1 || Hq % cache->Hkv != 0 || !(isfinite(scale) && scale > 0.f))
+    return SEPATTN_EINVAL;
+  const int G = Hq / cache->Hkv;
+  if (G > kMaxDecodeGroup || (G & (G - 1)) != 0) return SEPATTN_EUNSUPPORTED;
+  if (decode_workspace_bytes(*cache, Hq) > kNoAllocScratchBytes) return SEPATTN_ESCRATCH;
+  forget_stale_error();
+  return to_status(launch_decode_noalloc(*cache, q, Hq, rope_cos, rope_sin, scale, o, (hipStream_t)stream));
 }
 
 int sepcache_decode_profiled(const sepcache* cache, const void* q, int Hq, const float* rope_cos,

@@ -17,6 +17,8 @@
 // then V; the rotary angles of later passes come from one angle addition
 // per pass.  Cross-lane sums and maxima stay in registers (DPP, ds_swizzle,
 // v_permlane32_swap).
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace sepattn {
@@ -414,6 +416,50 @@ hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* 
   const int G = Hq / c.Hkv;
   if (c.d == 64) return launch_decode_d<64>(a, c.B, G, stream, ev);
   return launch_decode_d<128>(a, c.B, G, stream, ev);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the chunk partials go to a fixed array in device
+// memory instead of a caller workspace, for callers that cannot allocate
+// (code under graph capture, tight serving loops).  Every GPU the library runs
+// on holds its own copy of the array until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever passed to a kernel.  Every split of
+// the decode kernel writes its partial before the merge reads it, so nothing
+// needs clearing between calls; calls that overlap on one GPU share the array
+// and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+static hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const sepcache& c, const void* q, int Hq, const float* rope_cos,
+                                 const float* rope_sin, float scale, void* o, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_decode(c, q, Hq, rope_cos, rope_sin, scale, o, ws, stream, nullptr);
 }
 
 }  // namespace sepattn

@@ -44,5 +44,11 @@ size_t decode_workspace_bytes(const sepcache& c, int Hq);
 hipError_t launch_decode(const sepcache& c, const void* q, int Hq, const float* rope_cos,
                          const float* rope_sin, float scale, void* o, void* ws, hipStream_t stream,
                          hipEvent_t* ev);
+// Size of the library's fixed per-device scratch (the decode partials of
+// sepcache_decode_noalloc).
+constexpr size_t kNoAllocScratchBytes = SEPATTN_NOALLOC_SCRATCH_BYTES;
+// launch_decode with the fixed scratch as its workspace (callers check the size)
+hipError_t launch_decode_noalloc(const sepcache& c, const void* q, int Hq, const float* rope_cos,
+                                 const float* rope_sin, float scale, void* o, hipStream_t stream);
 
 }  // namespace sepattn

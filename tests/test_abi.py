@@ -163,6 +163,24 @@ def test_cache_hard_limits():
         assert ("128" in text) if st == 2 else ("8192" in text), text
 
 
+def test_noalloc_decode_host_checks():
+    """sepcache_decode_noalloc refuses, on the host, an input whose partials
+    would not fit the fixed scratch (ESCRATCH) and the usual bad arguments."""
+    L = sa.load_library()
+    fake = 1 << 40
+    fp = ctypes.c_void_p(fake)
+    z = ctypes.c_void_p(0)
+    c = sa._Cache(600, 8, 128, 800, 4, 64, 256, fake, fake, fake, fake, fake)
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 32) > (16 << 20)
+    assert L.sepcache_decode_noalloc(ctypes.byref(c), fp, 32, fp, fp, 0.1, fp, z) == 6
+    assert "scratch" in L.sepattn_strerror(6).decode()
+    c.B = 64
+    assert L.sepcache_decode_workspace(ctypes.byref(c), 32) <= (16 << 20)
+    assert L.sepcache_decode_noalloc(ctypes.byref(c), z, 32, fp, fp, 0.1, fp, z) == 1    # null q
+    assert L.sepcache_decode_noalloc(ctypes.byref(c), fp, 24, fp, fp, 0.1, fp, z) == 2   # group of 3
+    assert L.sepcache_decode_noalloc(ctypes.byref(c), fp, 32, fp, fp, -1.0, fp, z) == 1  # scale
+
+
 def test_rope_table_host_matches_double_precision():
     c, d, theta = 800, 128, 500000.0
     cos, sin = sa.rope_table(theta, c, d)
