@@ -224,16 +224,16 @@ def prefill_leg(args, torch, sa, synth):
     for s in range(K):
         step(marks[s])
     torch.cuda.synchronize()
-    names = ["index", "fwd", "bwd_rowsum", "bwd_main", "bwd_finalize"]
+    names = ["index", "fwd", "bwd_dq", "bwd_main", "bwd_finalize"]
     seg = {nm: [] for nm in names}
     for m in marks:
         seg["index"].append(ev.ms(m[0], m[1]))
         seg["fwd"].append(ev.ms(m[1], m[2]))
-        seg["bwd_rowsum"].append(ev.ms(m[3], m[4]))
+        seg["bwd_dq"].append(ev.ms(m[3], m[4]))
         seg["bwd_main"].append(ev.ms(m[4], m[5]))
         seg["bwd_finalize"].append(ev.ms(m[5], m[6]))
     avg = {nm: float(np.mean(x)) for nm, x in seg.items()}
-    dominant = max(("fwd", "bwd_main"), key=lambda k_: avg[k_])
+    dominant = max(("fwd", "bwd_dq", "bwd_main"), key=lambda k_: avg[k_])
 
     # timed region: K whole steps; events only around the dominant kernel
     dom = [ev.new(2) for _ in range(K)]
@@ -246,6 +246,8 @@ def prefill_leg(args, torch, sa, synth):
         if dominant == "fwd":
             ev.record(e2[1], stream)
             sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+        elif dominant == "bwd_dq":
+            sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws, events=[e2[0], e2[1], None, None])
         else:
             sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws, events=[None, e2[0], e2[1], None])
 
@@ -278,14 +280,17 @@ def prefill_leg(args, torch, sa, synth):
     ms_step = total_ms / K
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
-    # algorithmic work of each kernel (see the module docstring) and the
-    # GEMMs it executes per kept entry (backward main: S, dP, dV, dK
-    # key-major and S, dP, dQ query-major)
+    # algorithmic work of each kernel on the kept-tile schedule (see the
+    # module docstring): the GEMMs it computes per kept entry (forward: S,
+    # PV; backward dQ kernel: S, dP, dQ; backward main kernel, key-major: S,
+    # dP, dV, dK) and every tensor it reads once and writes once
     q_bytes, kv_bytes, row_bytes = B * Hq * S * d * 2, B * Hkv * S * d * 2, B * Hq * S * 4
-    kernel_flops = {"fwd": 4 * d * E, "bwd_main": 10 * d * E}
+    ld_bytes = B * Hq * ((S + 63) // 64) * 64 * 2 * 4   # per-row (log2e LSE, -D) of the dQ kernel
+    kernel_flops = {"fwd": 4 * d * E, "bwd_dq": 6 * d * E, "bwd_main": 8 * d * E}
     kernel_bytes = {"fwd": 2 * q_bytes + 2 * kv_bytes + row_bytes,
-                    "bwd_main": 3 * q_bytes + 4 * kv_bytes + 2 * row_bytes}
-    executed_flops = {"fwd": 4 * d * E, "bwd_main": 8 * d * (Ea + Eb) + 6 * d * E}
+                    "bwd_dq": 4 * q_bytes + 2 * kv_bytes + row_bytes + ld_bytes,
+                    "bwd_main": 2 * q_bytes + 4 * kv_bytes + ld_bytes}
+    executed_flops = kernel_flops
     t_mfma = kernel_flops[dominant] / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = kernel_bytes[dominant] / (PEAK_HBM_GBS * 1e9)
     tflops = kernel_flops[dominant] / (dom_ms * 1e-3) / 1e12
@@ -295,7 +300,7 @@ def prefill_leg(args, torch, sa, synth):
     hbm_view = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(gbs / PEAK_HBM_GBS, 4))
     binding, other = (hbm_view, mfma_view) if t_hbm >= t_mfma else (mfma_view, hbm_view)
-    kernel_symbol = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}[dominant]
+    kernel_symbol = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_main": "bwd_main_kernel"}[dominant]
     traffic = traffic_from_profiles(kernel_symbol)
     result = dict(
         metric="kept-tile TFLOP/s (fwd+bwd) and decode HBM GB/s; % of MI355X roofline",

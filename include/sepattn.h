@@ -180,13 +180,12 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
 /* sepattn_bwd with per-kernel timing: `events` is a HOST array of n_events
  * >= 4 hipEvent_t (created by the caller, passed as void*).  events[0] is
  * recorded on `stream` before the first kernel and events[i] after the i-th
- * of the three stages: (1) row sums D = rowsum(dO * O), (2) the main kernel
- * (key-major dK/dV over gathered anchor tiles and over band tiles, and
- * query-major dQ, as one grid of independent work items; for bf16 with
- * d = 128 the dQ items run as a second kernel right after it, and events[2]
- * follows both), (3) the sum of the anchor rows' partials.  A NULL entry
- * records nothing at its point.
- * Results are identical to sepattn_bwd. */
+ * of the three kernels: (1) query-major dQ, which also computes every row's
+ * D = rowsum(dO * O) for the next kernel, (2) the main kernel (key-major
+ * dK/dV over gathered anchor tiles and over band tiles, as one grid of
+ * independent work items), (3) the sum of the anchor rows' partials.  A NULL
+ * entry records nothing at its point.  Results are identical to
+ * sepattn_bwd. */
 int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
                          const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,

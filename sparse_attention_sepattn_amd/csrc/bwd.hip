@@ -9,15 +9,15 @@
 // dK/dV summed over the query heads of each kv group.
 //
 // Launches:
-//   pre      : D_i = rowsum(dO * O)
-//   main     : one grid of three kinds of independent work items, so the long
+//   dQ       : query-major dQ over the forward's schedule, one workgroup per
+//              query tile and head; each row's D = rowsum(dO * O) is computed
+//              from its O and dO rows here and stored with log2(e) LSE for
+//              the next kernel;
+//   main     : one grid of two kinds of independent work items, so the long
 //              anchor reductions run beside the short items instead of alone:
 //     anchor dK/dV -- key-major over gathered anchor tiles (128 anchors per
 //              workgroup); the query tiles are split into chunks and each
 //              (anchor tile, chunk) stores its fp32 partial in its own slot;
-//     dQ       -- query-major over the forward's schedule (bf16 at d=128:
-//              in a kernel of their own right after the main one, which fits
-//              two waves per SIMD where the key-major items fit one);
 //     band dK/dV -- key-major over 128-key tiles of the local band; a
 //              workgroup owns its rows: rows that are not anchors seen through
 //              the anchor path are scaled and stored in the input type, the
@@ -39,10 +39,6 @@ namespace sepattn {
 
 constexpr int kBwdThreads = 256;
 constexpr int kKeysPerWG = 128;  // 4 waves x 32 keys
-#ifndef SEPATTN_PRE_ROWS
-#define SEPATTN_PRE_ROWS 64
-#endif
-constexpr int kPreRows = SEPATTN_PRE_ROWS;  // rows of D per workgroup of the pre kernel
 
 // Workgroups per CU the register budget of the main kernel targets: the
 // d=128 and fp32 kernels keep more operands resident (key fragments and
@@ -68,22 +64,26 @@ constexpr int bwd_occupancy() {
 #ifndef SEPATTN_ANCHOR_ITEMS128
 #define SEPATTN_ANCHOR_ITEMS128 768
 #endif
-// bf16 dQ items in a kernel of their own after the main one, at SPLIT_OCC
-// waves per SIMD.  Measured on MI355X: 6% off the main backward at d=128
-// (8 kv heads of 32768); slower at d=64 (8x12 heads of 2048), where the dQ
-// items already share the main kernel's two waves per SIMD at no register cost.
-#ifndef SEPATTN_DQ_SPLIT
-#define SEPATTN_DQ_SPLIT 1
+// Waves per SIMD of the dQ kernel, and whether it uses the lean form (the
+// 32-key halves one after the other, K/V operands read in groups of 4, D
+// subtracted per score) that fits two waves per SIMD at d=128.
+#ifndef SEPATTN_DQ_OCC128
+#define SEPATTN_DQ_OCC128 2
 #endif
-#ifndef SEPATTN_DQ_SPLIT_OCC
-#define SEPATTN_DQ_SPLIT_OCC 2
+#ifndef SEPATTN_DQ_OCC64
+#define SEPATTN_DQ_OCC64 3
 #endif
-#ifndef SEPATTN_DQ_SPLIT64
-#define SEPATTN_DQ_SPLIT64 0
+#ifndef SEPATTN_DQ_LEAN64
+#define SEPATTN_DQ_LEAN64 1
 #endif
-#ifndef SEPATTN_DQ_SPLIT_OCC64
-#define SEPATTN_DQ_SPLIT_OCC64 3
-#endif
+template <typename T, int D>
+constexpr int dq_occupancy() {
+  return sizeof(T) == 2 ? (D == 64 ? SEPATTN_DQ_OCC64 : SEPATTN_DQ_OCC128) : 1;
+}
+template <typename T, int D>
+constexpr bool dq_lean() {
+  return sizeof(T) == 2 ? (D == 64 ? SEPATTN_DQ_LEAN64 != 0 : true) : true;
+}
 #ifndef SEPATTN_FIN_BLOCKS
 #define SEPATTN_FIN_BLOCKS 1024  // finalize workgroups in all (before the per-(b, kv head) floor of one)
 #endif
@@ -101,8 +101,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* Dvec;  // [B,Hq,S]
-  float* LD;    // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then -D (zero past S)
+  float* LD;  // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then -D (zero past S); written by the dQ items
   float* dKa;   // [nchunk+1,B,Hkv,S,D] fp32 partials by slot and anchor index
   float* dVa;
   const uint8_t* is_sep;
@@ -145,67 +144,6 @@ __device__ __forceinline__ int anchor_slot(const BwdArgs& p, int b, int krow, bo
   if (krow < n_init) ai = krow;
   else if (key_sep) ai = n_init + p.sep_prefix[(size_t)b * (p.S + 1) + krow];
   return (ai >= 0 && ai < n_last) ? ai : -1;
-}
-
-// ---------------------------------------------------------------------------
-// pre: D = rowsum(dO * O)
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs p) {
-  constexpr int VEC = Traits<T>::VEC;
-  constexpr int TPR = D / VEC;       // threads per row
-  constexpr int RPP = 256 / TPR;     // rows per pass of the workgroup
-  constexpr int NR = kPreRows / RPP;  // rows per thread, all loads in flight together
-  // rows of the 64-padded blocks of every (sequence, head)
-  const size_t rows_pad = (size_t)p.B * p.Hq * p.SB * kKTile;
-  const size_t per_bh = (size_t)p.SB * kKTile;
-  const int sub = threadIdx.x % TPR;
-  size_t prow[NR], row[NR];
-  bool valid[NR];
-  float acc[NR], lse[NR];
-  typedef typename std::conditional<VEC == 8, u32x4, f32x4>::type V4;
-  V4 ov[NR], gv[NR];
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    prow[k] = (size_t)blockIdx.x * kPreRows + k * RPP + threadIdx.x / TPR;
-    const size_t pr = prow[k] < rows_pad ? prow[k] : rows_pad - 1;
-    const size_t bh = pr / per_bh;
-    const int r = (int)(pr - bh * per_bh);
-    valid[k] = prow[k] < rows_pad && r < p.S;
-    row[k] = bh * p.S + (r < p.S ? r : 0);
-    ov[k] = *(const V4*)((const T*)p.o + row[k] * D + sub * VEC);
-    gv[k] = *(const V4*)((const T*)p.dout + row[k] * D + sub * VEC);
-    lse[k] = p.lse[row[k]];
-  }
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    float a = 0.f;
-    if constexpr (VEC == 8) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        a += __uint_as_float(ov[k][w] << 16) * __uint_as_float(gv[k][w] << 16);
-        a += __uint_as_float(ov[k][w] & 0xFFFF0000u) * __uint_as_float(gv[k][w] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a += ov[k][e] * gv[k][e];
-    }
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) a += __shfl_xor(a, off, 64);
-    acc[k] = a;
-  }
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    if (sub != 0 || prow[k] >= rows_pad) continue;
-    const size_t bh = prow[k] / per_bh;
-    const int r = (int)(prow[k] - bh * per_bh);
-    const float lse2 = valid[k] ? lse[k] * 1.4426950408889634f : 0.f;
-    const float d = valid[k] ? acc[k] : 0.f;
-    if (valid[k]) p.Dvec[row[k]] = d;
-    float* blk = p.LD + (bh * p.SB + r / kKTile) * (2 * kKTile);
-    blk[r % kKTile] = lse2;
-    blk[kKTile + r % kKTile] = -d;  // the dK/dV items start dP's accumulation from -D
-  }
 }
 
 // Double-buffered LDS tiles as separate arrays: each step names its buffer
@@ -617,7 +555,30 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     }
   }
   const float lse2 = q_ok ? p.lse[((size_t)b * p.Hq + h) * p.S + iq] * 1.4426950408889634f : 0.f;
-  const float Di = q_ok ? p.Dvec[((size_t)b * p.Hq + h) * p.S + iq] : 0.f;
+  // D_i = rowsum(dO * O)_i of this lane's row: the lane pair (l, l ^ 32)
+  // holds the row's two halves of dO; the same halves of O are loaded here
+  float Di = 0.f;
+  {
+    const T* Og = (const T*)p.o + qoff;
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) {
+      const frag oo = q_ok ? *(const frag*)(Og + (size_t)iq * D + c * KSTEP + EPL * hh) : frag{};
+      if constexpr (EPL == 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Di += (float)of[c][e] * (float)oo[e];
+      } else {
+        Di += of[c] * oo;
+      }
+    }
+    Di = pair_sum(Di);
+  }
+  // this row's (log2(e) LSE, -D) for the key-major items, which read them
+  // per 64-row block (rows past S, up to the block's end, get zeros)
+  if (hh == 0 && iq < p.SB * kKTile) {
+    float* blk = p.LD + (((size_t)b * p.Hq + h) * p.SB + iq / kKTile) * (2 * kKTile);
+    blk[iq % kKTile] = lse2;
+    blk[kKTile + iq % kKTile] = -Di;
+  }
   f32x16 negD;  // dP^T - D: every accumulation starts from -D of this lane's row
 #pragma unroll
   for (int i = 0; i < 16; ++i) negD[i] = -Di;
@@ -806,26 +767,20 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
     }
     return;
   }
-  x -= p.n_anchor_items;
-  if (x < p.n_dq_items) {
-    const int BH = p.B * p.Hq;
-    const int qi = p.QT - 1 - x / BH;
-    const int bh = x % BH;
-    dq_item<T, D>(p, bh / p.Hq, bh % p.Hq, qi, sm);
-    return;
-  }
   // band items: the units of one (sequence, kv head) share query tiles, so
   // keep each (sequence, kv head) on one XCD's L2
-  const int li = xcd_local_index(blockIdx.x, p.n_anchor_items + p.n_dq_items, p.n_band_items);
+  const int li = xcd_local_index(blockIdx.x, p.n_anchor_items, p.n_band_items);
   const int bg = li / p.units;
   const int unit = li - bg * p.units;
   dkdv_item<T, D, false>(p, bg / p.Hkv, bg % p.Hkv, unit, 0, sm);
 }
 
-// dQ items in a kernel of their own (d=128: the main kernel's key-major items
-// hold more registers than two waves per SIMD allow; the dQ items alone fit)
+// dQ items, the first kernel of the backward: they also produce every row's
+// D = rowsum(dO * O) (and log2(e) LSE) for the key-major items of the main
+// kernel.  A kernel of their own also fits more waves per SIMD than the
+// key-major items' registers allow.
 template <typename T, int D>
-__global__ void __launch_bounds__(kBwdThreads, D == 64 ? SEPATTN_DQ_SPLIT_OCC64 : SEPATTN_DQ_SPLIT_OCC) bwd_dq_kernel(BwdArgs p) {
+__global__ void __launch_bounds__(kBwdThreads, (dq_occupancy<T, D>())) bwd_dq_kernel(BwdArgs p) {
   typedef TileGeom<T, D> G;
   __shared__ __attribute__((aligned(16))) T smA0[G::ELEMS];
   __shared__ __attribute__((aligned(16))) T smA1[G::ELEMS];
@@ -836,7 +791,7 @@ __global__ void __launch_bounds__(kBwdThreads, D == 64 ? SEPATTN_DQ_SPLIT_OCC64 
   const int BH = p.B * p.Hq;
   const int qi = p.QT - 1 - x / BH;
   const int bh = x % BH;
-  dq_item<T, D, true>(p, bh / p.Hq, bh % p.Hq, qi, sm);
+  dq_item<T, D, dq_lean<T, D>()>(p, bh / p.Hq, bh % p.Hq, qi, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,33 +857,20 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   int nchunk, ct;
   anchor_split(B, Hkv, S, QT, d, &nchunk, &ct);
   const size_t SB = (S + kKTile - 1) / kKTile;
-  return a256((size_t)B * Hq * S * 4) + a256((size_t)B * Hq * SB * 2 * kKTile * 4) +
-         2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
+  return a256((size_t)B * Hq * SB * 2 * kKTile * 4) + 2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
 }
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
-  constexpr int TPR = D / Traits<T>::VEC;
-  const size_t rows = (size_t)a.B * a.Hq * a.SB * kKTile;  // 64-padded rows
-  const int pre_blocks = (int)((rows + kPreRows - 1) / kPreRows);
-  constexpr bool split = sizeof(T) == 2 && (D == 128 ? SEPATTN_DQ_SPLIT : SEPATTN_DQ_SPLIT64);
-  BwdArgs am = a;  // the main kernel's items (without the dQ items when they run apart)
-  if (split) am.n_dq_items = 0;
-  const int main_blocks = am.n_anchor_items + am.n_dq_items + am.n_band_items;
+  const int main_blocks = a.n_anchor_items + a.n_band_items;
   const int fin_rows_per_block = 256 / (D / 4);
   hipError_t e;
   if (ev && ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.n_dq_items), dim3(kBwdThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, am);
+  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3(main_blocks), dim3(kBwdThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if constexpr (split) {
-    if (a.n_dq_items > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.n_dq_items), dim3(kBwdThreads), 0, stream, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
   if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const int fin_x = std::max(1, std::min((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
                                          SEPATTN_FIN_BLOCKS / (a.B * a.Hkv)));
@@ -952,8 +894,6 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.dk = dk;
   a.dv = dv;
   char* w = (char*)ws;
-  a.Dvec = (float*)w;
-  w += a256((size_t)sh.B * sh.Hq * sh.S * 4);
   a.SB = (sh.S + kKTile - 1) / kKTile;
   a.LD = (float*)w;
   w += a256((size_t)sh.B * sh.Hq * a.SB * 2 * kKTile * 4);
