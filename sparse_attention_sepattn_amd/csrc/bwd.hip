@@ -16,13 +16,14 @@
 //   main     : one grid of two kinds of independent work items, so the long
 //              anchor reductions run beside the short items instead of alone:
 //     anchor dK/dV -- key-major over gathered anchor tiles (128 anchors per
-//              workgroup); the query tiles are split into chunks and each
-//              (anchor tile, chunk) stores its fp32 partial in its own slot;
-//     band dK/dV -- key-major over 128-key tiles of the local band; a
-//              workgroup owns its rows: rows that are not anchors seen through
-//              the anchor path are scaled and stored in the input type, the
-//              others store an fp32 partial in one more slot;
-//   finalize : rows that are anchors sum their slots and are stored.
+//              workgroup), every query row at or after each anchor (an
+//              initial token or a separator is seen by every later row); the
+//              query tiles are split into chunks by the shapes and, with more
+//              than one chunk, each (anchor tile, chunk) stores its fp32
+//              partial in its own slot, else the workgroup stores the rows;
+//     band dK/dV -- key-major over 128-key tiles of the local band for the
+//              keys that are not anchors; a workgroup owns and stores its rows;
+//   finalize : (several chunks only) anchor rows sum their slots and are stored.
 //
 // Key-major formulation: S = Q K^T with queries on the MFMA M axis and the
 // workgroup's keys on the N axis (lanes), so dV^T = dO^T P and dK^T = Q^T dS
@@ -102,11 +103,12 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* LD;  // [B,Hq,SB,128]: per 64-row block, log2(e)*LSE then -D (zero past S); written by the dQ items
-  float* dKa;   // [nchunk+1,B,Hkv,S,D] fp32 partials by slot and anchor index
+  float* dKa;   // [nchunk,B,Hkv,S,D] fp32 partials by chunk and anchor index (several chunks only)
   float* dVa;
   const uint8_t* is_sep;
   const int32_t* sep_prefix;
   const int32_t* anchor_pos;
+  const int32_t* anchor_count;
   const int32_t* qtile;
   int B, Hq, Hkv, S, a, n, QT;
   int SB;                   // ceil(S / 64) row blocks of LD
@@ -133,17 +135,6 @@ static void anchor_split(int B, int Hkv, int S, int QT, int d, int* nchunk, int*
   const int ct = (int)((QT + n - 1) / n);
   *chunk_tiles = ct;
   *nchunk = (QT + ct - 1) / ct;
-}
-
-// Anchor index of key row `krow` if it is an anchor that some query sees
-// through the anchor path (index below the last query tile's anchor count),
-// else -1.
-__device__ __forceinline__ int anchor_slot(const BwdArgs& p, int b, int krow, bool key_sep, int n_last) {
-  const int n_init = p.a < p.S ? p.a : p.S;
-  int ai = -1;
-  if (krow < n_init) ai = krow;
-  else if (key_sep) ai = n_init + p.sep_prefix[(size_t)b * (p.S + 1) + krow];
-  return (ai >= 0 && ai < n_last) ? ai : -1;
 }
 
 // Double-buffered LDS tiles as separate arrays: each step names its buffer
@@ -181,22 +172,20 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   const int hh = lane >> 5;
   const int kc = lane & 31;
   const int grp = p.Hq / p.Hkv;
-  const int32_t* qt = p.qtile + (size_t)b * p.QT * kQF;
-  const int n_last = qt[(p.QT - 1) * kQF + 1];
-
   int qi_begin, qi_end;  // query-tile range [qi_begin, qi_end)
   if constexpr (ANCHOR) {
-    // Query tile qi sees anchor number j iff anchor_pos[j] < lo(qi) =
-    // max(0, 128 qi - n + 1): the first tile that sees this unit's first
-    // anchor (position p0) is (p0 + n - 1) / 128 + 1.
+    // Every row at or after an anchor's position sees it (an initial token or
+    // a separator: through the gathered anchor tiles, or within its window
+    // through the band), so the anchor items take the whole column of every
+    // anchor and the band items leave anchors out.  The unit's rows start at
+    // the query tile that holds its first anchor (position p0).
     const int a0 = unit * kKeysPerWG;
     const int p0 = a0 < p.S ? p.anchor_pos[(size_t)b * p.S + a0] : -1;
-    const int first = p0 >= 0 ? (p0 + p.n - 1) / kQTile + 1 : p.QT;
-    if (first >= p.QT) return false;  // no query sees these anchors (nor later ones); never read
-    qi_begin = max(first, chunk * p.chunk_tiles);
+    if (p0 < 0) return false;  // past the last anchor, as are the units after it
+    qi_begin = max(p0 / kQTile, chunk * p.chunk_tiles);
     qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);
-    // no query tile of this chunk sees the unit: nothing to add, and the
-    // finalize never reads this chunk's slot for these anchors
+    // no row of this chunk sees the unit: nothing to add, and the finalize
+    // never reads this chunk's slot for these anchors
     if (qi_begin >= qi_end) return true;
   } else {
     const int k0 = unit * kKeysPerWG;
@@ -210,14 +199,16 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   // this lane's key
   const int kidx = unit * kKeysPerWG + 32 * w + kc;  // key row (band) or anchor index (anchor)
   int krow;
-  // (anchor-list entries past the anchor count are -1; anchors at or past
-  // n_last get zero weight from the visibility test and their slots are
-  // never read)
+  // (anchor-list entries past the anchor count are -1)
   if constexpr (ANCHOR) krow = kidx < p.S ? p.anchor_pos[(size_t)b * p.S + kidx] : -1;
   else krow = kidx < p.S ? kidx : -1;
-  const bool key_sep = (!ANCHOR && krow >= 0) ? (p.is_sep[(size_t)b * p.S + krow] != 0) : false;
-  // band: last row that sees this key (all later rows for initial / separator keys)
-  const int q_hi = (krow < p.a || key_sep) ? p.S - 1 : min(p.S - 1, krow + p.n - 1);
+  // band: anchors (initial tokens and separators) are the anchor items' keys
+  const bool key_anchor =
+      (!ANCHOR && krow >= 0) ? (krow < p.a || p.is_sep[(size_t)b * p.S + krow] != 0) : false;
+  // rows [krow, q_hi] see this lane's key: every later row for an anchor,
+  // the window for a band key
+  const int q_hi = ANCHOR ? p.S - 1 : min(p.S - 1, krow + p.n - 1);
+  const bool key_live = krow >= 0 && !key_anchor;
 
   const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
   const T* Vg = (const T*)p.v + (((size_t)b * p.Hkv + g) * p.S) * D;
@@ -248,11 +239,6 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
                                              16, off, 0, 0, 0);
   };
 
-  // anchor items: anchor count of each step's query tile, loaded one step
-  // ahead into the slot of the step's buffer parity
-  auto anchor_count_of = [&](int it) { return qt[(it_row0(it) / kQTile) * kQF + 1]; };
-  int nlim[2] = {0, 0};
-  if (ANCHOR && n_it > 0) nlim[0] = anchor_count_of(0);
   if (n_it > 0) issue(0, Buf0{});
 
   // this lane's key rows (a lane without a key reads row 0: its column is
@@ -284,23 +270,11 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     wait_vm_all();    // this wave's part of tile `it` (and its LSE/D copy) has landed in LDS
     __syncthreads();  // tile `it` visible; every wave is done with tile it-1's buffer
     const int r0 = it_row0(it);
-    const int qi = r0 / kQTile;
     if (it + 1 < n_it) issue(it + 1, std::integral_constant<int, 1 - buf>{});
-    // the anchor count of the next step's query tile, read now and used there
-    if constexpr (ANCHOR) nlim[1 - buf] = anchor_count_of(min(it + 1, n_it - 1));
 
     // query-row range [ql, qh] of the rows that see this lane's key
-    int ql, qh;
-    if constexpr (ANCHOR) {
-      const bool seen = krow >= 0 && kidx < nlim[buf];
-      ql = seen ? 0 : 1;
-      qh = seen ? p.S - 1 : 0;
-    } else {
-      // window start of the query tile (the index builder's lo)
-      const bool in_band = krow >= 0 && krow >= max(0, qi * kQTile - p.n + 1);
-      ql = in_band ? krow : 1;
-      qh = in_band ? q_hi : 0;
-    }
+    const int ql = key_live ? krow : 1;
+    const int qh = key_live ? q_hi : 0;
     // every row of this 64-row chunk sees every key of the wave: skip the tests
     const bool full = __all(ql <= r0 && qh >= r0 + kKTile - 1);
     // bit r: row r0 + r sees this lane's key
@@ -399,26 +373,22 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     if (it < n_it) step(it, Buf0{});
   }
 
-  // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i)
-  if (krow < 0) return true;
+  // epilogue: this lane holds column kidx of dK^T / dV^T, rows d = 32db + acc_row(i).
+  // A band key's column and, with one chunk, an anchor's are complete and
+  // stored in the input type; with several chunks an anchor's column is an
+  // fp32 partial in the chunk's slot, summed by the finalize kernel.
+  if (!key_live) return true;
   float* ka = nullptr;
   float* va = nullptr;
   T* dkg = nullptr;
   T* dvg = nullptr;
-  if constexpr (ANCHOR) {
+  if (ANCHOR && p.nchunk > 1) {
     const size_t off = (((size_t)chunk * p.B + b) * p.Hkv + g) * p.S + kidx;
     ka = p.dKa + off * D;
     va = p.dVa + off * D;
   } else {
-    const int ai = anchor_slot(p, b, krow, key_sep, n_last);
-    if (ai >= 0) {
-      const size_t off = (((size_t)p.nchunk * p.B + b) * p.Hkv + g) * p.S + ai;
-      ka = p.dKa + off * D;
-      va = p.dVa + off * D;
-    } else {
-      dkg = (T*)p.dk + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
-      dvg = (T*)p.dv + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
-    }
+    dkg = (T*)p.dk + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
+    dvg = (T*)p.dv + (((size_t)b * p.Hkv + g) * p.S + krow) * D;
   }
 #pragma unroll
   for (int dbk = 0; dbk < NDB; ++dbk)
@@ -795,41 +765,40 @@ __global__ void __launch_bounds__(kBwdThreads, (dq_occupancy<T, D>())) bwd_dq_ke
 }
 
 // ---------------------------------------------------------------------------
-// finalize: anchor rows = sum of their partial slots, stored in the input type
+// finalize (several anchor chunks only): anchor rows = sum of their partial
+// slots, stored in the input type
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdArgs p) {
   constexpr int TPR = D / 4;  // threads per row, 4 elements each
   const int bg = blockIdx.y;
   const int b = bg / p.Hkv;
-  const int n_last = p.qtile[((size_t)b * p.QT + p.QT - 1) * kQF + 1];
+  const int n_anchor = p.anchor_count[b];
   const int c4 = (threadIdx.x % TPR) * 4;
   const size_t cstride = (size_t)p.B * p.Hkv * p.S * D;
   // the anchor count is known on the device only: a fixed number of
   // workgroups per (sequence, kv head) strides over it
-  for (int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR; ai < n_last; ai += gridDim.x * (256 / TPR)) {
+  for (int ai = blockIdx.x * (256 / TPR) + threadIdx.x / TPR; ai < n_anchor; ai += gridDim.x * (256 / TPR)) {
     const size_t off = ((size_t)bg * p.S + ai) * D + c4;
     const int krow = p.anchor_pos[(size_t)b * p.S + ai];
-    // the anchor-path chunks that hold a query tile seeing this anchor (the
-    // first such tile is the first whose window starts after it; earlier
-    // chunks' slots were not written), then the band slot
-    const int first = (krow + p.n - 1) / kQTile + 1;
-    const int cmin = min(first / p.chunk_tiles, p.nchunk);
+    // the chunks that hold a row at or after the anchor (earlier chunks'
+    // slots were not written)
+    const int cmin = min((krow / kQTile) / p.chunk_tiles, p.nchunk - 1);
     f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-    // the partials of 4 slots in flight at once (slots past nchunk re-read
-    // the last one and are not added)
-    for (int c0 = cmin; c0 <= p.nchunk; c0 += 4) {
+    // the partials of 4 slots in flight at once (slots past the last re-read
+    // it and are not added)
+    for (int c0 = cmin; c0 < p.nchunk; c0 += 4) {
       f32x4 k4[4], v4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const size_t cc = (size_t)min(c0 + j, p.nchunk);
+        const size_t cc = (size_t)min(c0 + j, p.nchunk - 1);
         k4[j] = *(const f32x4*)(p.dKa + cc * cstride + off);
         v4[j] = *(const f32x4*)(p.dVa + cc * cstride + off);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool use = c0 + j <= p.nchunk;
+        const bool use = c0 + j < p.nchunk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sk[e] += use ? k4[j][e] : 0.f;
@@ -857,7 +826,10 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   int nchunk, ct;
   anchor_split(B, Hkv, S, QT, d, &nchunk, &ct);
   const size_t SB = (S + kKTile - 1) / kKTile;
-  return a256((size_t)B * Hq * SB * 2 * kKTile * 4) + 2 * a256((size_t)(nchunk + 1) * B * Hkv * S * d * 4);
+  // per-row (log2(e) LSE, -D); then, with several anchor chunks, one fp32
+  // partial slot per chunk for dK and for dV
+  return a256((size_t)B * Hq * SB * 2 * kKTile * 4) +
+         (nchunk > 1 ? 2 * a256((size_t)nchunk * B * Hkv * S * d * 4) : 0);
 }
 
 template <typename T, int D>
@@ -874,8 +846,10 @@ static hipError_t launch_bwd_t(BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
   if (ev && ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const int fin_x = std::max(1, std::min((a.S + fin_rows_per_block - 1) / fin_rows_per_block,
                                          SEPATTN_FIN_BLOCKS / (a.B * a.Hkv)));
-  hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3(fin_x, a.B * a.Hkv), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.nchunk > 1) {
+    hipLaunchKernelGGL((bwd_finalize_kernel<T, D>), dim3(fin_x, a.B * a.Hkv), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev && ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -899,12 +873,13 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   w += a256((size_t)sh.B * sh.Hq * a.SB * 2 * kKTile * 4);
   a.QT = (sh.S + kQTile - 1) / kQTile;
   anchor_split(sh.B, sh.Hkv, sh.S, a.QT, sh.d, &a.nchunk, &a.chunk_tiles);
-  a.dKa = (float*)w;
-  w += a256((size_t)(a.nchunk + 1) * sh.B * sh.Hkv * sh.S * sh.d * 4);
-  a.dVa = (float*)w;
+  a.dKa = a.nchunk > 1 ? (float*)w : nullptr;
+  w += a.nchunk > 1 ? a256((size_t)a.nchunk * sh.B * sh.Hkv * sh.S * sh.d * 4) : 0;
+  a.dVa = a.nchunk > 1 ? (float*)w : nullptr;
   a.is_sep = idx.is_sep;
   a.sep_prefix = idx.sep_prefix;
   a.anchor_pos = idx.anchor_pos;
+  a.anchor_count = idx.anchor_count;
   a.qtile = idx.qtile;
   a.B = sh.B;
   a.Hq = sh.Hq;
