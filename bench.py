@@ -18,19 +18,19 @@ measured step time (index build included).  The useful-entry count
 
 roofline: the kernel with the largest average duration (its duration measured
 with HIP events on the launch stream during the timed steps), placed by its
-algorithmic work: FLOPs on the same schedule (forward 4*d*E; backward 10*d*E,
-the FlashAttention-2 count with one recompute of S) and bytes (every input
-tensor read once and every output written once: the forward reads Q, K, V
-and writes O and the LSE; the backward main kernel reads Q, K, V, dO, the
-LSE and D and writes dQ, dK, dV).  Whichever takes longer at the MI355X peak
-(bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) is the bound reported; the other
-view is given beside it.  The FLOPs the kernel executes (its dQ items
-recompute S and dP: 14*d*E) are reported too.
+algorithmic work on the kept-tile schedule: the GEMMs it computes per kept
+entry (forward: S and PV, 4*d*E; backward dQ kernel: S, dP and dQ, 6*d*E;
+backward main kernel, key-major: S, dP, dV and dK, 8*d*E) and the bytes of
+every tensor it reads once and writes once.  Whichever takes longer at the
+MI355X peak (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) is the bound reported;
+the other view is given beside it.
 
 other_configs: the d=128 shapes (Llama-3-8B-shaped prefill, B1 32/8 heads,
-8192 tokens, n=256; 32768 tokens with bursty separators), whole steps and
-the forward alone, kept-tile TFLOP/s on the same counting; reported beside
-the main workload, not part of its value (--no-long skips them).
+8192 tokens, n=256; 32768 tokens with bursty separators), whole steps timed,
+then every kernel timed with events in a second pass; kept-tile TFLOP/s on
+the same counting, and a roofline block for the step's dominant kernel and
+one for the forward; reported beside the main workload, not part of its
+value (--no-long skips them).
 
 decode: the streaming SepCache workload (B=64, 32 q / 8 kv heads, d=128,
 c=800 = 4 initial + 64 separator slots + a 256-token window, RoPE theta
@@ -157,6 +157,43 @@ TRAFFIC_SOURCE = ("profiles/traffic.json: FETCH_SIZE and WRITE_SIZE from two roc
                   "source hash matches)")
 
 
+def kernel_work(B, Hq, Hkv, S, d, E):
+    """Algorithmic work of each kernel on the kept-tile schedule (bf16): the
+    GEMMs it computes per kept entry (forward: S, PV; backward dQ kernel: S,
+    dP, dQ; backward main kernel, key-major: S, dP, dV, dK) and every tensor
+    it reads once and writes once."""
+    q_bytes, kv_bytes, row_bytes = B * Hq * S * d * 2, B * Hkv * S * d * 2, B * Hq * S * 4
+    ld_bytes = B * Hq * ((S + 63) // 64) * 64 * 2 * 4   # per-row (log2e LSE, -D) of the dQ kernel
+    flops = {"fwd": 4 * d * E, "bwd_dq": 6 * d * E, "bwd_main": 8 * d * E}
+    nbytes = {"fwd": 2 * q_bytes + 2 * kv_bytes + row_bytes,
+              "bwd_dq": 4 * q_bytes + 2 * kv_bytes + row_bytes + ld_bytes,
+              "bwd_main": 2 * q_bytes + 4 * kv_bytes + ld_bytes}
+    return flops, nbytes
+
+
+KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_main": "bwd_main_kernel"}
+
+
+def roofline_block(kernel, avg_ms, flops, nbytes, traffic=None):
+    """The kernel placed by its algorithmic work: whichever of its flops (at
+    the bf16 MFMA peak) and bytes (at the HBM peak) takes longer is the
+    bound; achieved = that work / the average launch time."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    mfma_view = dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                     frac=round(tflops / PEAK_BF16_TFLOPS, 4))
+    hbm_view = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(gbs / PEAK_HBM_GBS, 4))
+    binding, other = (hbm_view, mfma_view) if t_hbm >= t_mfma else (mfma_view, hbm_view)
+    return dict(kernel=KERNEL_SYMBOL[kernel], **binding, traffic=traffic,
+                traffic_source=TRAFFIC_SOURCE if traffic else None,
+                algorithmic_mb_per_launch=round(nbytes / 1e6, 3), algorithmic_gflop_per_launch=round(flops / 1e9, 3),
+                time_at_peak_us=dict(hbm=round(t_hbm * 1e6, 2), mfma=round(t_mfma * 1e6, 2)),
+                other_view=other, avg_launch_ms=round(avg_ms, 5))
+
+
 def traffic_from_profiles(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a known-size copy), if it was taken
@@ -280,28 +317,9 @@ def prefill_leg(args, torch, sa, synth):
     ms_step = total_ms / K
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
-    # algorithmic work of each kernel on the kept-tile schedule (see the
-    # module docstring): the GEMMs it computes per kept entry (forward: S,
-    # PV; backward dQ kernel: S, dP, dQ; backward main kernel, key-major: S,
-    # dP, dV, dK) and every tensor it reads once and writes once
-    q_bytes, kv_bytes, row_bytes = B * Hq * S * d * 2, B * Hkv * S * d * 2, B * Hq * S * 4
-    ld_bytes = B * Hq * ((S + 63) // 64) * 64 * 2 * 4   # per-row (log2e LSE, -D) of the dQ kernel
-    kernel_flops = {"fwd": 4 * d * E, "bwd_dq": 6 * d * E, "bwd_main": 8 * d * E}
-    kernel_bytes = {"fwd": 2 * q_bytes + 2 * kv_bytes + row_bytes,
-                    "bwd_dq": 4 * q_bytes + 2 * kv_bytes + row_bytes + ld_bytes,
-                    "bwd_main": 2 * q_bytes + 4 * kv_bytes + ld_bytes}
-    executed_flops = kernel_flops
-    t_mfma = kernel_flops[dominant] / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = kernel_bytes[dominant] / (PEAK_HBM_GBS * 1e9)
-    tflops = kernel_flops[dominant] / (dom_ms * 1e-3) / 1e12
-    gbs = kernel_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-    mfma_view = dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                     frac=round(tflops / PEAK_BF16_TFLOPS, 4))
-    hbm_view = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(gbs / PEAK_HBM_GBS, 4))
-    binding, other = (hbm_view, mfma_view) if t_hbm >= t_mfma else (mfma_view, hbm_view)
-    kernel_symbol = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_main": "bwd_main_kernel"}[dominant]
-    traffic = traffic_from_profiles(kernel_symbol)
+    kernel_flops, kernel_bytes = kernel_work(B, Hq, Hkv, S, d, E)
+    traffic = traffic_from_profiles(KERNEL_SYMBOL[dominant])
+    roof = roofline_block(dominant, dom_ms, kernel_flops[dominant], kernel_bytes[dominant], traffic)
     result = dict(
         metric="kept-tile TFLOP/s (fwd+bwd) and decode HBM GB/s; % of MI355X roofline",
         value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=K, warmup=args.warmup,
@@ -313,14 +331,10 @@ def prefill_leg(args, torch, sa, synth):
                     useful_gflop_fwd_bwd=round(14 * d * nnz / 1e9, 3), tile_efficiency=round(nnz / E, 4),
                     wall_ms_per_step=round(wall / K * 1e3, 4)),
         kernels_ms_untimed_pass={nm: round(x, 5) for nm, x in avg.items()},
-        roofline=dict(kernel=kernel_symbol, **binding, traffic=traffic, traffic_source=TRAFFIC_SOURCE if traffic else None,
-                      algorithmic_mb_per_launch=round(kernel_bytes[dominant] / 1e6, 3),
-                      algorithmic_gflop_per_launch=round(kernel_flops[dominant] / 1e9, 3),
-                      executed_gflop_per_launch=round(executed_flops[dominant] / 1e9, 3),
-                      time_at_peak_us=dict(hbm=round(t_hbm * 1e6, 2), mfma=round(t_mfma * 1e6, 2)),
-                      other_view=other, avg_launch_ms=round(dom_ms, 5)),
+        roofline=roof,
     )
-    result["dense_layer"] = dense_layer(args, torch, sa, (q, k, v, do), tok, sep, scale, cfg, ev_cls=Events)
+    if not args.no_dense:
+        result["dense_layer"] = dense_layer(args, torch, sa, (q, k, v, do), tok, sep, scale, cfg, ev_cls=Events)
     return result, inp, E_seqs
 
 
@@ -429,9 +443,8 @@ def long_configs(args, torch, sa, synth):
             if fe is not None:
                 ev.record(fe[0], stream)
             sa.fwd(q, k, v, idx, scale, o=o, lse=lse)
-            if fe is not None:
-                ev.record(fe[1], stream)
-            sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+            sa.bwd(q, k, v, o, lse, do, idx, scale, dq=dq, dk=dk, dv=dv, ws=ws,
+                   events=None if fe is None else fe[1:5])
 
         for _ in range(3):
             step()
@@ -443,20 +456,29 @@ def long_configs(args, torch, sa, synth):
         ev.record(t1, stream)
         torch.cuda.synchronize()
         ms_step = ev.ms(t0, t1) / steps
-        fmarks = [ev.new(2) for _ in range(steps)]
+        # per kernel: events before the forward and around the backward's
+        # kernels (dQ, main, finalize) in a second pass, not the timed one
+        fmarks = [ev.new(5) for _ in range(steps)]
         for fe in fmarks:
             step(fe)
         torch.cuda.synchronize()
-        ms_fwd = float(np.mean([ev.ms(fe[0], fe[1]) for fe in fmarks]))
+        kms = {nm: float(np.mean([ev.ms(fe[i], fe[i + 1]) for fe in fmarks]))
+               for i, nm in enumerate(("fwd", "bwd_dq", "bwd_main", "bwd_finalize"))}
         ev.close()
         qtile = idx.qtile.cpu().numpy()
         pref = idx.sep_prefix.cpu().numpy()
         E = sum(schedule_counts(qtile[b], pref[b], a, n, S)[0] for b in range(B)) * Hq
+        flops, nbytes = kernel_work(B, Hq, Hkv, S, d, E)
+        dominant = max(("fwd", "bwd_dq", "bwd_main"), key=lambda k_: kms[k_])
+        ms_fwd = kms["fwd"]
         fwd_tf = 4 * d * E / (ms_fwd * 1e-3) / 1e12
         out[name] = dict(B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, a=a, n=n, bursty=bool(cfg.get("bursty")),
                          steps=steps, ms_per_step=round(ms_step, 4), fwd_ms=round(ms_fwd, 4),
                          kept_tile_TFLOPs_fwd_bwd=round(14 * d * E / (ms_step * 1e-3) / 1e12, 3),
-                         fwd_TFLOPs=round(fwd_tf, 3), fwd_frac_of_mfma_peak=round(fwd_tf / PEAK_BF16_TFLOPS, 4))
+                         fwd_TFLOPs=round(fwd_tf, 3), fwd_frac_of_mfma_peak=round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                         kernels_ms_untimed_pass={k_: round(v_, 5) for k_, v_ in kms.items()},
+                         roofline=roofline_block(dominant, kms[dominant], flops[dominant], nbytes[dominant]),
+                         fwd_roofline=roofline_block("fwd", ms_fwd, flops["fwd"], nbytes["fwd"]))
         del q, k, v, do, o, lse, dq, dk, dv, ws, idx, tok
         torch.cuda.empty_cache()
     return out
@@ -707,6 +729,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the d=128 Llama-shaped and 32k-token steps")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-layer (window n = S) steps of the Pythia-shaped leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first launch one device-to-device copy of this many MiB (a known-size kernel "
