@@ -518,6 +518,8 @@ def decode_leg(args, torch, sa, synth):
     nb = min(T, args.decode_breakdown_steps)
     ring = EventRing(ev, 4)
     for t in range(nb):
+        if t and t % 1024 == 0:
+            log(f"  decode breakdown pass: step {t}")
         m = ring.take()
         ev.record(m[0], stream)
         cache.update(ks[t], vs[t], toks[t], sep)
@@ -541,9 +543,12 @@ def decode_leg(args, torch, sa, synth):
 
     # the decode kernel alone, cache-warm: the same steps with an event pair
     # around every decode kernel (read back in groups, outside the kernels)
+    log("  decode timed pass done")
     cache.init()
     ring = EventRing(ev, 2)
     for t in range(T):
+        if t and t % 1024 == 0:
+            log(f"  decode cache-warm pass: step {t}")
         cache.update(ks[t], vs[t], toks[t], sep)
         m = ring.take()
         cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[m[0], m[1], None])
@@ -565,6 +570,8 @@ def decode_leg(args, torch, sa, synth):
     ring = EventRing(ev, 2, depth=64)
     torch.cuda.synchronize()
     for t in range(T):
+        if t and t % 1024 == 0:
+            log(f"  decode flushed pass: step {t}")
         cache.update(ks[t], vs[t], toks[t], sep)
         if t in sampled_set:
             torch.sum(scratch, dim=(0,), out=flush_sink)
