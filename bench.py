@@ -506,6 +506,8 @@ def decode_leg(args, torch, sa, synth):
     # untimed pass: cache lengths after every update (for the byte count)
     lens = torch.empty((T, B, 4), dtype=torch.int32, device=dev)
     for t in range(T):
+        if t and t % 1024 == 0:
+            log(f"  decode length pass: step {t}")
         cache.update(ks[t], vs[t], toks[t], sep)
         lens[t].copy_(cache.state)
     L = lens[:, :, :3].sum(-1).cpu().numpy().astype(np.int64)  # [T, B]
@@ -515,7 +517,8 @@ def decode_leg(args, torch, sa, synth):
 
     # per-kernel breakdown (events between every kernel); not the timed region
     cache.init()
-    nb = min(T, args.decode_breakdown_steps)
+    only_flushed = args.decode_flushed_only
+    nb = 0 if only_flushed else min(T, args.decode_breakdown_steps)
     ring = EventRing(ev, 4)
     for t in range(nb):
         if t and t % 1024 == 0:
@@ -529,30 +532,32 @@ def decode_leg(args, torch, sa, synth):
     upd = np.array([x[0] for x in bt][lob:])
     mrg = np.array([x[2] for x in bt][lob:])
 
-    # timed region: T update + decode steps, events only at its ends
-    cache.init()
-    t0, t1 = ev.new(2)
-    torch.cuda.synchronize()
-    ev.record(t0, stream)
-    for t in range(T):
-        cache.update(ks[t], vs[t], toks[t], sep)
-        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws)
-    ev.record(t1, stream)
-    torch.cuda.synchronize()
-    total_ms = ev.ms(t0, t1)
+    total_ms = dec = None
+    if not only_flushed:
+        # timed region: T update + decode steps, events only at its ends
+        cache.init()
+        t0, t1 = ev.new(2)
+        torch.cuda.synchronize()
+        ev.record(t0, stream)
+        for t in range(T):
+            cache.update(ks[t], vs[t], toks[t], sep)
+            cache.decode(qs[t], cos, sin, scale, o=out, ws=ws)
+        ev.record(t1, stream)
+        torch.cuda.synchronize()
+        total_ms = ev.ms(t0, t1)
 
-    # the decode kernel alone, cache-warm: the same steps with an event pair
-    # around every decode kernel (read back in groups, outside the kernels)
-    log("  decode timed pass done")
-    cache.init()
-    ring = EventRing(ev, 2)
-    for t in range(T):
-        if t and t % 1024 == 0:
-            log(f"  decode cache-warm pass: step {t}")
-        cache.update(ks[t], vs[t], toks[t], sep)
-        m = ring.take()
-        cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[m[0], m[1], None])
-    dec = np.array([x[0] for x in ring.result()])
+        # the decode kernel alone, cache-warm: the same steps with an event pair
+        # around every decode kernel (read back in groups, outside the kernels)
+        log("  decode timed pass done")
+        cache.init()
+        ring = EventRing(ev, 2)
+        for t in range(T):
+            if t and t % 1024 == 0:
+                log(f"  decode cache-warm pass: step {t}")
+            cache.update(ks[t], vs[t], toks[t], sep)
+            m = ring.take()
+            cache.decode(qs[t], cos, sin, scale, o=out, ws=ws, events=[m[0], m[1], None])
+        dec = np.array([x[0] for x in ring.result()])
 
     # flushed pass: at every 8th step of the steady state, reading 512 MB of
     # scratch evicts the K/V working set (at most ~210 MB here, below the
@@ -588,10 +593,11 @@ def decode_leg(args, torch, sa, synth):
     q_bytes = B * Hq * d * 2
     table_bytes = c * (d // 2) * 4 * 2
     dec_bytes = kv_bytes + q_bytes + table_bytes            # per decode-kernel launch
-    gbs_warm = dec_bytes[lo:].sum() / (dec[lo:].sum() * 1e-3) / 1e9
     gbs = dec_bytes[sampled].sum() / (fdec.sum() * 1e-3) / 1e9   # flushed: the HBM figure
     step_bytes = kv_bytes + 2 * q_bytes + B * Hkv * d * 2 * 2 + B * 4
-    step_ms = total_ms / T
+    rnd = lambda x, k: None if x is None else round(float(x), k)  # noqa: E731
+    gbs_warm = None if dec is None else dec_bytes[lo:].sum() / (dec[lo:].sum() * 1e-3) / 1e9
+    step_ms = None if total_ms is None else total_ms / T
     traffic = traffic_from_profiles("decode_kernel")
     return dict(
         workload="SepCache streaming decode: B64, 32 q / 8 kv heads, d128, bf16, c=800 (a4 s64 w256), "
@@ -599,14 +605,14 @@ def decode_leg(args, torch, sa, synth):
         steps=T, steady_from=lo, mean_cached_slots=round(float(L[lo:].mean()), 1),
         decode_kernel_us_flushed=round(float(fdec.mean()) * 1e3, 3),
         flushed_launches=len(sampled),
-        decode_kernel_us_cache_warm=round(float(dec[lo:].mean()) * 1e3, 3),
-        cache_warm_GBps=round(float(gbs_warm), 1),
+        decode_kernel_us_cache_warm=None if dec is None else round(float(dec[lo:].mean()) * 1e3, 3),
+        cache_warm_GBps=rnd(gbs_warm, 1),
         merge_kernel_us_untimed_pass=round(float(mrg.mean()) * 1e3, 3) if nb else None,
         update_kernel_us_untimed_pass=round(float(upd.mean()) * 1e3, 3) if nb else None,
-        us_per_step=round(step_ms * 1e3, 3), loop_ms_total=round(total_ms, 3),
+        us_per_step=None if step_ms is None else round(step_ms * 1e3, 3), loop_ms_total=rnd(total_ms, 3),
         value=round(float(gbs), 1), unit="GB/s",
         prefill_handoff=handoff,
-        step_GBps=round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
+        step_GBps=None if total_ms is None else round(float(step_bytes.sum() / (total_ms * 1e-3) / 1e9), 1),
         roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(float(gbs), 1), peak=PEAK_HBM_GBS,
                       unit="GB/s", frac=round(float(gbs) / PEAK_HBM_GBS, 4), traffic=traffic,
                       traffic_source=TRAFFIC_SOURCE if traffic else None,
@@ -734,6 +740,9 @@ def main():
     ap.add_argument("--decode-breakdown-steps", type=int, default=1024,
                     help="steps of the untimed per-kernel breakdown pass of the decode leg (0: none)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-flushed-only", action="store_true",
+                    help="decode leg: only the length pass and the flushed pass (for counter runs, whose "
+                         "per-dispatch overhead makes every pass slow)")
     ap.add_argument("--no-long", action="store_true", help="skip the d=128 Llama-shaped and 32k-token steps")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
