@@ -759,9 +759,10 @@ __global__ void __launch_bounds__(kBwdThreads, (dq_occupancy<T, D>())) bwd_dq_ke
   const SmemBufs<T> sm = {{smA0, smA1}, {smB0, smB1}, {nullptr, nullptr}};
   const int x = blockIdx.x;
   const int BH = p.B * p.Hq;
-  const int qi = p.QT - 1 - x / BH;
-  const int bh = x % BH;
-  dq_item<T, D, dq_lean<T, D>()>(p, bh / p.Hq, bh % p.Hq, qi, sm);
+  const int qi = p.QT - 1 - x / BH;  // heaviest query tiles (most anchors) first
+  int b, h;
+  query_column(x % BH, p.B, p.Hq, p.Hkv, b, h);
+  dq_item<T, D, dq_lean<T, D>()>(p, b, h, qi, sm);
 }
 
 // ---------------------------------------------------------------------------

@@ -78,4 +78,18 @@ __device__ __forceinline__ int xcd_local_index(int g, int base, int n) {
   return before + ((g - base) - first) / kXcd;
 }
 
+// Sequence b and query head h of query-major work column x in [0, B*Hq).
+// Workgroups are dealt to the 8 XCDs round-robin by launch index and each XCD
+// has its own L2: the columns are ordered so that the query heads of one
+// (sequence, kv head) are B*Hkv columns apart, which puts them all on one
+// XCD whenever B*Hkv and B*Hq are multiples of 8 (then the XCD of a column
+// is its (sequence, kv head) mod 8).  The K/V tiles those heads share are then
+// read from HBM once per XCD instead of once per head.
+__device__ __forceinline__ void query_column(int x, int B, int Hq, int Hkv, int& b, int& h) {
+  const int BG = B * Hkv, grp = Hq / Hkv;
+  const int bg = x % BG, j = x / BG;
+  b = bg / Hkv;
+  h = (bg - b * Hkv) * grp + j;
+}
+
 }  // namespace sepattn

@@ -81,9 +81,8 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
 
   // heaviest query tiles (most anchors) are dispatched first
   const int qi = p.QT - 1 - (int)blockIdx.y;
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
+  int b, h;
+  query_column(blockIdx.x, p.B, p.Hq, p.Hkv, b, h);
   const int g = h / (p.Hq / p.Hkv);
 
   // Band tiles first (their rows follow from q0 and n), gathered anchor tiles
