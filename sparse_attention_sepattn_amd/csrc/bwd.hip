@@ -172,29 +172,32 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   const int hh = lane >> 5;
   const int kc = lane & 31;
   const int grp = p.Hq / p.Hkv;
-  int qi_begin, qi_end;  // query-tile range [qi_begin, qi_end)
+  int rb_begin, rb_end;  // 64-row query blocks [rb_begin, rb_end) the item steps through
   if constexpr (ANCHOR) {
     // Every row at or after an anchor's position sees it (an initial token or
     // a separator: through the gathered anchor tiles, or within its window
     // through the band), so the anchor items take the whole column of every
     // anchor and the band items leave anchors out.  The unit's rows start at
-    // the query tile that holds its first anchor (position p0).
+    // the block that holds its first anchor (position p0); a chunk is a range
+    // of query tiles.
     const int a0 = unit * kKeysPerWG;
     const int p0 = a0 < p.S ? p.anchor_pos[(size_t)b * p.S + a0] : -1;
     if (p0 < 0) return false;  // past the last anchor, as are the units after it
-    qi_begin = max(p0 / kQTile, chunk * p.chunk_tiles);
-    qi_end = min(p.QT, (chunk + 1) * p.chunk_tiles);
+    constexpr int BPQ = kQTile / kKTile;  // 64-row blocks per query tile
+    rb_begin = max(p0 / kKTile, chunk * p.chunk_tiles * BPQ);
+    rb_end = min(p.SB, (chunk + 1) * p.chunk_tiles * BPQ);
     // no row of this chunk sees the unit: nothing to add, and the finalize
     // never reads this chunk's slot for these anchors
-    if (qi_begin >= qi_end) return true;
+    if (rb_begin >= rb_end) return true;
   } else {
+    // rows [k0, k1 + n - 1]: the windows of the unit's keys
     const int k0 = unit * kKeysPerWG;
     const int k1 = min(k0 + kKeysPerWG - 1, p.S - 1);
-    qi_begin = k0 / kQTile;
-    qi_end = min(p.QT, (k1 + p.n - 1) / kQTile + 1);
+    rb_begin = k0 / kKTile;
+    rb_end = min(p.S - 1, k1 + p.n - 1) / kKTile + 1;
   }
-  const int n_q = max(0, qi_end - qi_begin);
-  const int n_it = grp * n_q * 2;  // (query head, query tile, 64-row half)
+  const int n_rb = max(0, rb_end - rb_begin);
+  const int n_it = grp * n_rb;  // (query head, 64-row block)
 
   // this lane's key
   const int kidx = unit * kKeysPerWG + 32 * w + kc;  // key row (band) or anchor index (anchor)
@@ -213,11 +216,8 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
   const T* Vg = (const T*)p.v + (((size_t)b * p.Hkv + g) * p.S) * D;
 
-  auto it_head = [&](int it) { return g * grp + it / (2 * n_q); };
-  auto it_row0 = [&](int it) {
-    const int r = it % (2 * n_q);
-    return (qi_begin + (r >> 1)) * kQTile + (r & 1) * kKTile;
-  };
+  auto it_head = [&](int it) { return g * grp + it / n_rb; };
+  auto it_row0 = [&](int it) { return (rb_begin + it % n_rb) * kKTile; };
   const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
   // Q and dO tiles of step `it` straight into LDS buffer B
