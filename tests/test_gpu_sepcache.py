@@ -61,7 +61,12 @@ def test_golden_trace_on_gpu(golden):
 
 
 def _stream_run(B, Hkv, Hq, d, c, a, s, w, steps, p_sep, seed, check_every=1, decode_every=0,
-                theta=500000.0):
+                theta=500000.0, rows_every=None, on_fire=True):
+    """Stream `steps` tokens into a GPU cache and the oracle's simulations.
+    Positions, ids and counters are compared every `check_every` steps (and
+    on every compression if `on_fire`), the K/V rows too every `rows_every`
+    steps (default: at every such check); decode every `decode_every`
+    steps (and on compressions if `on_fire`) against the oracle."""
     import sparse_attention_sepattn_amd as sa
     cfg = dict(seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d, vocab=5000, p_sep=p_sep)
     stream = synth.DecodeStream(cfg)
@@ -82,9 +87,11 @@ def _stream_run(B, Hkv, Hq, d, c, a, s, w, steps, p_sep, seed, check_every=1, de
             fb = sims[b].append(x["tok"][b], x["k"][b], x["v"][b])
             compressions[b] += int(fb)
             fired |= fb
-        if fired or t % check_every == 0 or t == steps - 1:
-            _compare_cache(cache, sims, Hkv, d, c, full_rows=True, where=f"t={t}")
-        if decode_every and (t % decode_every == 0 or fired or t == steps - 1):
+        fire = fired and on_fire
+        if fire or t % check_every == 0 or t == steps - 1:
+            rows = rows_every is None or t % rows_every == 0 or t == steps - 1
+            _compare_cache(cache, sims, Hkv, d, c, full_rows=rows, where=f"t={t}")
+        if decode_every and (t % decode_every == 0 or fire or t == steps - 1):
             o = host_f64(cache.decode(dev_tensor(x["q"], "bf16"), cos_d, sin_d, scale))
             for b in range(B):
                 slots = sims[b].slots()
@@ -128,6 +135,22 @@ def test_streaming_decode_config_prefix():
                             check_every=100, decode_every=100, theta=cfg["theta"])
     say(f"decode config: compressions per sequence min={nc.min()} max={nc.max()} decode max err={worst:.3g}")
     assert nc.min() == 2 and nc.max() == 2
+    assert worst <= 2e-2
+
+
+def test_streaming_decode_config_full_length():
+    """The streaming-decode configuration over its whole 4096 steps (every
+    sequence compresses 7 to 8 times): positions, ids and counters bit-exact
+    every 64 steps, K/V rows every 1024 steps and at the end, decode checked
+    every 256 steps against the oracle."""
+    require_gpu()
+    cfg = synth.CONFIGS["sepcache_decode"]
+    worst, nc = _stream_run(B=cfg["B"], Hkv=cfg["Hkv"], Hq=cfg["Hq"], d=cfg["d"], c=cfg["c"], a=cfg["a"],
+                            s=cfg["s"], w=cfg["w"], steps=cfg["steps"], p_sep=cfg["p_sep"], seed=cfg["seed"],
+                            check_every=64, decode_every=256, theta=cfg["theta"], rows_every=1024, on_fire=False)
+    say(f"decode config, 4096 steps: compressions per sequence min={nc.min()} max={nc.max()} "
+        f"decode max err={worst:.3g}")
+    assert nc.min() >= 6
     assert worst <= 2e-2
 
 
