@@ -36,7 +36,7 @@ constexpr float kLazy = 8.f;
 #define SEPATTN_FWD_SKIP 1  // skip 32-key halves no query of the wave sees
 #endif
 #ifndef SEPATTN_FWD_OCC
-#define SEPATTN_FWD_OCC 3  // workgroups per CU the bf16 d=64 register budget targets (4 spills at 4)
+#define SEPATTN_FWD_OCC 4  // waves per SIMD the bf16 d=64 register budget targets (128 VGPRs, no spills)
 #endif
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)

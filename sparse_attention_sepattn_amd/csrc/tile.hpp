@@ -134,7 +134,9 @@ struct TileDMA {
   static constexpr int NU = R::NU;
   static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned src_bytes, const int* srow,
                                                T* tile, int tid) {
-    const int w = tid / kWave, lane = tid % kWave;
+    // the wave index is uniform: read it into a scalar so the LDS destination
+    // (M0) of every load is a scalar value, not a per-lane one read back
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int pos = tid % G::CH;  // 16-byte position of this lane in its LDS row
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -144,7 +146,6 @@ struct TileDMA {
       const unsigned off = srow[u] >= 0 ? (unsigned)(srow[u] * D + c * Traits<T>::VEC) * (unsigned)sizeof(T)
                                         : src_bytes;
       T* dst = tile + (w * 1024 + u * NT * 16) / (int)sizeof(T);
-      (void)lane;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
     }
   }
