@@ -116,6 +116,7 @@ struct BwdArgs {
   int units;                // ceil(S / 128) key units per (sequence, kv head)
   int anchor_lanes;         // anchor work items per (sequence, kv head, chunk); each walks units
                             // lane, lane + anchor_lanes, ... until one has no anchor a query sees
+  int anchor_stride;        // B * Hkv * nchunk rounded up to a multiple of 8: anchor items per lane
   int n_anchor_items, n_dq_items, n_band_items;
   float scale;
   float scale_log2;
@@ -216,8 +217,19 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
   const T* Kg = (const T*)p.k + (((size_t)b * p.Hkv + g) * p.S) * D;
   const T* Vg = (const T*)p.v + (((size_t)b * p.Hkv + g) * p.S) * D;
 
-  auto it_head = [&](int it) { return g * grp + it / n_rb; };
-  auto it_row0 = [&](int it) { return (rb_begin + it % n_rb) * kKTile; };
+  // Step order.  Anchor items walk the row blocks from the chunk's last one
+  // down, the query heads inside: every anchor unit of a (sequence, kv head,
+  // chunk) then reads the same Q/dO tiles at the same step, while they run
+  // side by side on one XCD, so a tile comes from HBM once for all of them
+  // (they differ only in where they stop).  Band items: head by head.
+  auto it_head = [&](int it) {
+    if constexpr (ANCHOR) return g * grp + it % grp;
+    else return g * grp + it / n_rb;
+  };
+  auto it_row0 = [&](int it) {
+    if constexpr (ANCHOR) return (rb_end - 1 - it / grp) * kKTile;
+    else return (rb_begin + it % n_rb) * kKTile;
+  };
   const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
   // Q and dO tiles of step `it` straight into LDS buffer B
@@ -725,10 +737,12 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   int x = blockIdx.x;
   const int BG = p.B * p.Hkv;
   if (x < p.n_anchor_items) {
-    // lane-major so the first anchor units come first
-    const int per_lane = BG * p.nchunk;
-    const int lane0 = x / per_lane;
-    const int r = x - lane0 * per_lane;
+    // lane-major so the first anchor units come first; a lane's items are
+    // padded to a multiple of the 8 XCDs (anchor_stride), so that every lane
+    // of one (sequence, kv head, chunk) runs on the same XCD
+    const int lane0 = x / p.anchor_stride;
+    const int r = x - lane0 * p.anchor_stride;
+    if (r >= BG * p.nchunk) return;
     const int bg = r / p.nchunk;
     const int chunk = r - bg * p.nchunk;
     for (int unit = lane0; unit < p.units; unit += p.anchor_lanes) {
@@ -890,7 +904,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.n = idx.n < idx.S ? idx.n : idx.S;  // as the index builders store it
   a.units = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
   a.anchor_lanes = std::min(a.units, std::max(2, sh.S / 2048));
-  a.n_anchor_items = a.anchor_lanes * sh.B * sh.Hkv * a.nchunk;
+  a.anchor_stride = (sh.B * sh.Hkv * a.nchunk + 7) / 8 * 8;
+  a.n_anchor_items = a.anchor_lanes * a.anchor_stride;
   a.n_dq_items = sh.B * sh.Hq * a.QT;
   a.n_band_items = a.units * sh.B * sh.Hkv;
   a.scale = sh.scale;
