@@ -230,18 +230,21 @@ __device__ __forceinline__ bool dkdv_item(const BwdArgs& p, int b, int g, int un
     if constexpr (ANCHOR) return (rb_end - 1 - it / grp) * kKTile;
     else return (rb_begin + it % n_rb) * kKTile;
   };
-  const unsigned qbytes = (unsigned)((size_t)p.S * D * sizeof(T));
   const unsigned ldbytes = (unsigned)((size_t)p.SB * 2 * kKTile * sizeof(float));
+  unsigned uoff[Regs::NU];
+#pragma unroll
+  for (int u = 0; u < Regs::NU; ++u) uoff[u] = tile_unit_offset<T, D, kBwdThreads>(tid, u);
   // Q and dO tiles of step `it` straight into LDS buffer B
   auto issue = [&](int it, auto B) {
     constexpr int buf = decltype(B)::value;
     const int h = it_head(it);
     const int r0 = it_row0(it);
     const size_t bh = (size_t)b * p.Hq + h;
-    int rows[Regs::NU];
-    Regs::rows(rows, RowSrc{nullptr, r0, p.S}, tid);
-    DMA::issue(buffer_rsrc((const T*)p.q + bh * p.S * D, qbytes), qbytes, rows, sm.a[buf], tid);
-    DMA::issue(buffer_rsrc((const T*)p.dout + bh * p.S * D, qbytes), qbytes, rows, sm.b[buf], tid);
+    // consecutive rows r0 ..: a resource from row r0 to the end, constant offsets
+    const size_t rbase = (bh * p.S + r0) * D;
+    const unsigned rbytes = (unsigned)((size_t)(p.S - r0) * D * sizeof(T));
+    DMA::issue_rows(buffer_rsrc((const T*)p.q + rbase, rbytes), uoff, sm.a[buf], tid);
+    DMA::issue_rows(buffer_rsrc((const T*)p.dout + rbase, rbytes), uoff, sm.b[buf], tid);
     // this wave's own copy of the tile's 64 (log2(e)*LSE, -D) pairs: lanes
     // 0..31 carry the 512-byte block, lanes 32..63 read past the buffer
     // (zeros into the unused half of the wave's 1 KB slot)
@@ -506,24 +509,37 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     }
   };
   // K and V tiles of tile t straight into LDS buffer B (its separator
-  // flags, for band tiles, into sflag)
+  // flags, for band tiles, into sflag).  Band tiles (consecutive rows) use
+  // per-thread constant offsets into a buffer resource that starts at the
+  // tile; anchor tiles take their rows from the list.
+  unsigned uoff[Regs::NU];
+#pragma unroll
+  for (int u = 0; u < Regs::NU; ++u) uoff[u] = tile_unit_offset<T, D, kBwdThreads>(tid, u);
   int sflag = 0;
   auto issue = [&](int t, auto B) {
     constexpr int buf = decltype(B)::value;
-    int rows[Regs::NU];
-    if (t > 0) resolve(t, rows);
-    else Regs::rows(rows, src_of(t), tid);
-    DMA::issue(Krs, kv_bytes, rows, sm.a[buf], tid);
-    DMA::issue(Vrs, kv_bytes, rows, sm.b[buf], tid);
     sflag = 0;
-    if (t < n_band) {
-      const int j = (kb + t) * kKTile + lane;
+    if (t < n_band) {  // wave-uniform
+      const int r0 = (kb + t) * kKTile;
+      const unsigned bytes = (unsigned)((size_t)(p.S - r0) * D * sizeof(T));
+      DMA::issue_rows(buffer_rsrc(Kg + (size_t)r0 * D, bytes), uoff, sm.a[buf], tid);
+      DMA::issue_rows(buffer_rsrc(Vg + (size_t)r0 * D, bytes), uoff, sm.b[buf], tid);
+      const int j = r0 + lane;
       sflag = j < p.S ? (int)sepf[j] : 0;
+    } else {
+      int rows[Regs::NU];
+      resolve(t, rows);
+      DMA::issue(Krs, kv_bytes, rows, sm.a[buf], tid);
+      DMA::issue(Vrs, kv_bytes, rows, sm.b[buf], tid);
     }
   };
+  // the anchor-list entries of anchor tiles only
+  auto fetch_anchor = [&](int t) {
+    if (t >= n_band) fetch(t);
+  };
 
-  issue(0, Buf0{});
-  fetch(min(1, n_tiles - 1));
+  issue(0, Buf0{});  // a band tile
+  fetch_anchor(min(1, n_tiles - 1));
 
   frag qf[NQF], of[NQF];
 #pragma unroll
@@ -582,7 +598,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     __syncthreads();
     if (t + 1 < n_tiles) {
       issue(t + 1, std::integral_constant<int, 1 - buf>{});
-      fetch(min(t + 2, n_tiles - 1));
+      fetch_anchor(min(t + 2, n_tiles - 1));
     }
 
     const bool anchor_tile = t >= n_band;

@@ -143,19 +143,34 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   };
 
   // tile t straight into LDS buffer B (its separator flags, for band tiles,
-  // into sflag)
+  // into sflag).  A band tile's rows are consecutive: its loads use
+  // per-thread constant offsets into a buffer resource that starts at the
+  // tile (scalar work per tile); an anchor tile's rows come from the list.
+  unsigned uoff[Regs::NU];
+#pragma unroll
+  for (int u = 0; u < Regs::NU; ++u) uoff[u] = tile_unit_offset<T, D, kFwdThreads>(tid, u);
   int sflag = 0;
   auto issue = [&](int t, auto B) {
-    int rows[Regs::NU];
-    if (t > 0) resolve(t, rows);
-    else Regs::rows(rows, src_of(t), tid);
-    DMA::issue(Krs, kv_bytes, rows, kbuf(B), tid);
-    DMA::issue(Vrs, kv_bytes, rows, vbuf(B), tid);
+    if (t < n_band) {  // wave-uniform
+      const int r0 = (kb + t) * kKTile;
+      const unsigned bytes = (unsigned)((size_t)(p.S - r0) * D * sizeof(T));
+      DMA::issue_rows(buffer_rsrc(Kg + (size_t)r0 * D, bytes), uoff, kbuf(B), tid);
+      DMA::issue_rows(buffer_rsrc(Vg + (size_t)r0 * D, bytes), uoff, vbuf(B), tid);
+    } else {
+      int rows[Regs::NU];
+      resolve(t, rows);
+      DMA::issue(Krs, kv_bytes, rows, kbuf(B), tid);
+      DMA::issue(Vrs, kv_bytes, rows, vbuf(B), tid);
+    }
     sflag = sep_flag(t);
   };
-  // prologue: tile 0 in flight, the anchor rows of tile 1 requested
+  // the anchor-list entries of anchor tiles only
+  auto fetch_anchor = [&](int t) {
+    if (t >= n_band) fetch(t);
+  };
+  // prologue: tile 0 (a band tile) in flight, the anchor rows of tile 1 requested
   issue(0, I0);
-  fetch(min(1, n_tiles - 1));
+  fetch_anchor(min(1, n_tiles - 1));
 
   frag qf[NQF];
 #pragma unroll
@@ -182,7 +197,7 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
     if (t + 1 < n_tiles) {
       issue(t + 1, NB);  // the next tile fills the other buffer
-      fetch(min(t + 2, n_tiles - 1));
+      fetch_anchor(min(t + 2, n_tiles - 1));
     }
     const T* K = kbuf(B);
     const T* V = vbuf(B);

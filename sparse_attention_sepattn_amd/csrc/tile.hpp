@@ -149,7 +149,32 @@ struct TileDMA {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
     }
   }
+  // A tile of 64 consecutive rows: `src` starts at the tile's first row and
+  // ends where the tensor ends, so rows past the end read zeros; the offsets
+  // are the per-thread constants of tile_unit_offset, and only the resource
+  // (scalar) changes from tile to tile.
+  static __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t src, const unsigned* uoff, T* tile,
+                                                    int tid) {
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      T* dst = tile + (w * 1024 + u * NT * 16) / (int)sizeof(T);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, uoff[u], 0, 0,
+                                               0);
+    }
+  }
 };
+
+// Byte offset, within a tile of consecutive rows, of the 16-byte chunk that
+// thread tid's unit u loads (TileDMA's layout): a per-thread constant.
+template <typename T, int D, int NT>
+__device__ __forceinline__ unsigned tile_unit_offset(int tid, int u) {
+  typedef TileGeom<T, D> G;
+  const int r = TileRows<T, D, NT>::row_of(tid, u);
+  const int f = G::CH >= 16 ? swz16(r) : swz8(r);
+  const int c = ((tid % G::CH) ^ f) & (G::CH - 1);
+  return (unsigned)(r * D + c * Traits<T>::VEC) * (unsigned)sizeof(T);
+}
 
 // Buffer resource over `bytes` bytes from `base` (raw, no stride).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
