@@ -264,7 +264,7 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
     const float m_use = m == -INFINITY ? 0.f : m;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4] = {-0.f, -0.f, -0.f, -0.f};  // -0 + x = x exactly, so the first adds fold away
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       if (!live[k2]) continue;
