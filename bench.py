@@ -194,17 +194,18 @@ def roofline_block(kernel, avg_ms, flops, nbytes, traffic=None):
                 other_view=other, avg_launch_ms=round(avg_ms, 5))
 
 
-def traffic_from_profiles(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a known-size copy), if it was taken
-    on the current kernel sources; else None."""
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` (a synth.CONFIGS name)
+    from the committed counter summary (FETCH_SIZE and WRITE_SIZE, scaled by
+    a known-size copy), if it was taken on the current kernel sources; else
+    None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         import hashlib
         with open(path) as f:
-            rec = json.load(f).get(kernel)
+            rec = json.load(f).get(workload, {}).get(kernel)
         if not rec:
             return None
         h = hashlib.sha256()
@@ -318,7 +319,7 @@ def prefill_leg(args, torch, sa, synth):
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
     kernel_flops, kernel_bytes = kernel_work(B, Hq, Hkv, S, d, E)
-    traffic = traffic_from_profiles(KERNEL_SYMBOL[dominant])
+    traffic = traffic_from_profiles(KERNEL_SYMBOL[dominant], "pythia160m")
     roof = roofline_block(dominant, dom_ms, kernel_flops[dominant], kernel_bytes[dominant], traffic)
     result = dict(
         metric="kept-tile TFLOP/s (fwd+bwd) and decode HBM GB/s; % of MI355X roofline",
@@ -477,8 +478,10 @@ def long_configs(args, torch, sa, synth):
                          kept_tile_TFLOPs_fwd_bwd=round(14 * d * E / (ms_step * 1e-3) / 1e12, 3),
                          fwd_TFLOPs=round(fwd_tf, 3), fwd_frac_of_mfma_peak=round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                          kernels_ms_untimed_pass={k_: round(v_, 5) for k_, v_ in kms.items()},
-                         roofline=roofline_block(dominant, kms[dominant], flops[dominant], nbytes[dominant]),
-                         fwd_roofline=roofline_block("fwd", ms_fwd, flops["fwd"], nbytes["fwd"]))
+                         roofline=roofline_block(dominant, kms[dominant], flops[dominant], nbytes[dominant],
+                                                 traffic_from_profiles(KERNEL_SYMBOL[dominant], name)),
+                         fwd_roofline=roofline_block("fwd", ms_fwd, flops["fwd"], nbytes["fwd"],
+                                                     traffic_from_profiles("fwd_kernel", name)))
         del q, k, v, do, o, lse, dq, dk, dv, ws, idx, tok
         torch.cuda.empty_cache()
     return out
@@ -598,7 +601,7 @@ def decode_leg(args, torch, sa, synth):
     rnd = lambda x, k: None if x is None else round(float(x), k)  # noqa: E731
     gbs_warm = None if dec is None else dec_bytes[lo:].sum() / (dec[lo:].sum() * 1e-3) / 1e9
     step_ms = None if total_ms is None else total_ms / T
-    traffic = traffic_from_profiles("decode_kernel")
+    traffic = traffic_from_profiles("decode_kernel", "sepcache_decode")
     return dict(
         workload="SepCache streaming decode: B64, 32 q / 8 kv heads, d128, bf16, c=800 (a4 s64 w256), "
                  "RoPE theta 500000 by slot, p_sep 0.08; value: decode kernel after reading 512 MB (cache flush)",
