@@ -183,9 +183,11 @@ int sepattn_bwd(const void* q, const void* k, const void* v, const void* o, cons
  * of the three kernels: (1) query-major dQ, which also computes every row's
  * D = rowsum(dO * O) for the next kernel, (2) the main kernel (key-major
  * dK/dV over gathered anchor tiles and over band tiles, as one grid of
- * independent work items), (3) the sum of the anchor rows' partials.  A NULL
- * entry records nothing at its point.  Results are identical to
- * sepattn_bwd. */
+ * independent work items), (3) the sum of the anchor rows' partials, which
+ * runs only when the anchor columns are split over several chunks of query
+ * tiles (with one chunk the main kernel stores them and events[3] directly
+ * follows events[2]).  A NULL entry records nothing at its point.  Results
+ * are identical to sepattn_bwd. */
 int sepattn_bwd_profiled(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, int B, int Hq, int Hkv, int S, int d, int dtype, float scale,
                          const sepattn_index* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
