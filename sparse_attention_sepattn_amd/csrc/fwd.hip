@@ -38,6 +38,9 @@ constexpr float kLazy = 8.f;
 #ifndef SEPATTN_FWD_OCC
 #define SEPATTN_FWD_OCC 4  // waves per SIMD the bf16 d=64 register budget targets (128 VGPRs, no spills)
 #endif
+#ifndef SEPATTN_FWD_QLDS
+#define SEPATTN_FWD_QLDS 1  // the query tile comes in through LDS (coalesced rows)
+#endif
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
 #endif
@@ -173,10 +176,29 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   fetch_anchor(min(1, n_tiles - 1));
 
   frag qf[NQF];
+#if SEPATTN_FWD_QLDS
+  if constexpr (EPL == 8) {
+    // The query tile comes in through the second pair of tile buffers (free
+    // until tile 1 is issued) as two 64-row tiles, with the same coalesced
+    // row loads as K and V, and each wave reads its 32 rows' fragments back;
+    // rows past the end read zeros.
+    const int rest = p.S - q0;
+    DMA::issue_rows(buffer_rsrc(Qg + (size_t)q0 * D, (unsigned)(rest * D * sizeof(T))), uoff, Ks1, tid);
+    const unsigned hi = rest > kKTile ? (unsigned)((rest - kKTile) * D * sizeof(T)) : 0u;
+    DMA::issue_rows(buffer_rsrc(Qg + (size_t)min(q0 + kKTile, p.S - 1) * D, hi), uoff, Vs1, tid);
+    wait_vm_all();
+    __syncthreads();
+    const T* Qt = w < 2 ? Ks1 : Vs1;
 #pragma unroll
-  for (int c = 0; c < NQF; ++c) {
-    if (q_ok) qf[c] = *(const frag*)(Qg + (size_t)iq * D + c * KSTEP + EPL * hh);
-    else qf[c] = frag{};
+    for (int c = 0; c < NQF; ++c) qf[c] = read_x<T, D>(Qt, w & 1, c, lane);
+  } else
+#endif
+  {
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) {
+      if (q_ok) qf[c] = *(const frag*)(Qg + (size_t)iq * D + c * KSTEP + EPL * hh);
+      else qf[c] = frag{};
+    }
   }
 
   f32x16 oacc[NDB];
@@ -307,6 +329,47 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   // normalise and store
   const float l_tot = pair_sum(l);
   const float inv = 1.f / l_tot;
+#if SEPATTN_FWD_QLDS
+  if constexpr (EPL == 8) {
+    // O goes out as whole rows: each wave puts its 32 rows into the first
+    // pair of tile buffers (row-major, swizzled like every tile), then every
+    // thread stores the 16-byte chunks a tile load would have brought in
+    // from those rows (consecutive lanes, consecutive chunks of a row).
+    __syncthreads();  // every wave is done with the last tile's buffers
+    T* Ot = w < 2 ? Ks0 : Vs0;
+    const int orow = 32 * (w & 1) + qc;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * db + 8 * r4 + 4 * hh;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+        pk[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *(u32x2*)(Ot + G::at(orow, d0)) = pk;
+      }
+    }
+    __syncthreads();
+    T* Ob = (T*)p.o + ((size_t)b * p.Hq + h) * p.S * D;
+    const int wu = __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const T* src = half == 0 ? Ks0 : Vs0;
+#pragma unroll
+      for (int u = 0; u < Regs::NU; ++u) {
+        const int r = Regs::row_of(tid, u);
+        const int grow = q0 + kKTile * half + r;
+        const u32x4 v = *(const u32x4*)(src + (wu * 1024 + u * kFwdThreads * 16) / (int)sizeof(T) + lane * 8);
+        if (grow < p.S) *(u32x4*)(Ob + (size_t)grow * D + uoff[u] / sizeof(T) - (size_t)r * D) = v;
+      }
+    }
+    if (q_ok && hh == 0) {
+      // natural-log normaliser of the scaled scores
+      p.lse[((size_t)b * p.Hq + h) * p.S + iq] = (m + fast_log2(l_tot)) * 0.69314718055994530942f;
+    }
+    return;
+  }
+#endif
   if (q_ok) {
     T* Og = (T*)p.o + (((size_t)b * p.Hq + h) * p.S + iq) * D;
 #pragma unroll
