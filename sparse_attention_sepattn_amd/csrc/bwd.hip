@@ -712,6 +712,15 @@ __device__ __forceinline__ void dq_item(const BwdArgs& p, int b, int h, int qi, 
     if (t < n_tiles) step(t, Buf0{});
   }
 
+  if constexpr (EPL == 8) {
+    // dQ goes out as whole rows through the first pair of tile buffers
+    __syncthreads();  // every wave is done with the last tile's buffers
+    T* dQb = (T*)p.dq + qoff + (size_t)q0 * D;
+    const int nrows = p.S - q0;
+    store_rows_via_lds<D, kBwdThreads>(sm.a[0], sm.b[0], dq, p.scale,
+                                       [&](int r) { return r < nrows ? dQb + (size_t)r * D : nullptr; }, uoff, tid);
+    return;
+  }
   if (q_ok) {
     T* dQg = (T*)p.dq + qoff + (size_t)iq * D;
 #pragma unroll

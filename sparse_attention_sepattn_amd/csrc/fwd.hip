@@ -336,33 +336,10 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
     // thread stores the 16-byte chunks a tile load would have brought in
     // from those rows (consecutive lanes, consecutive chunks of a row).
     __syncthreads();  // every wave is done with the last tile's buffers
-    T* Ot = w < 2 ? Ks0 : Vs0;
-    const int orow = 32 * (w & 1) + qc;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * db + 8 * r4 + 4 * hh;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
-        pk[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *(u32x2*)(Ot + G::at(orow, d0)) = pk;
-      }
-    }
-    __syncthreads();
-    T* Ob = (T*)p.o + ((size_t)b * p.Hq + h) * p.S * D;
-    const int wu = __builtin_amdgcn_readfirstlane(tid / kWave);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const T* src = half == 0 ? Ks0 : Vs0;
-#pragma unroll
-      for (int u = 0; u < Regs::NU; ++u) {
-        const int r = Regs::row_of(tid, u);
-        const int grow = q0 + kKTile * half + r;
-        const u32x4 v = *(const u32x4*)(src + (wu * 1024 + u * kFwdThreads * 16) / (int)sizeof(T) + lane * 8);
-        if (grow < p.S) *(u32x4*)(Ob + (size_t)grow * D + uoff[u] / sizeof(T) - (size_t)r * D) = v;
-      }
-    }
+    T* Ob = (T*)p.o + (((size_t)b * p.Hq + h) * p.S + q0) * D;
+    const int nrows = p.S - q0;
+    store_rows_via_lds<D, kFwdThreads>(Ks0, Vs0, oacc, inv, [&](int r) { return r < nrows ? Ob + (size_t)r * D : nullptr; },
+                                       uoff, tid);
     if (q_ok && hh == 0) {
       // natural-log normaliser of the scaled scores
       p.lse[((size_t)b * p.Hq + h) * p.S + iq] = (m + fast_log2(l_tot)) * 0.69314718055994530942f;

@@ -176,6 +176,50 @@ __device__ __forceinline__ unsigned tile_unit_offset(int tid, int u) {
   return (unsigned)(r * D + c * Traits<T>::VEC) * (unsigned)sizeof(T);
 }
 
+// A 128-row block of bf16 output held transposed in MFMA accumulators (wave
+// w: rows 32w .. 32w+31, lane = row within those 32; acc[db] element i =
+// column 32db + acc_row(i, lane / 32), times `scale`) goes out as whole rows:
+// the waves write their rows into two 64-row tiles (A: rows 0..63, B: rows
+// 64..127, swizzled like every tile), then every thread stores the 16-byte
+// chunks that a tile load (TileDMA) would have brought into its LDS slots, so
+// consecutive lanes store consecutive chunks of a row.  row_dst(r) gives the
+// destination of block row r (nullptr: not stored).  The caller's barrier
+// must precede the call (both tiles free); the tiles are overwritten.
+template <int D, int NT, typename RowDst>
+__device__ __forceinline__ void store_rows_via_lds(__bf16* tileA, __bf16* tileB, const f32x16* acc, float scale,
+                                                   RowDst row_dst, const unsigned* uoff, int tid) {
+  typedef TileGeom<__bf16, D> G;
+  typedef TileRows<__bf16, D, NT> R;
+  constexpr int NDB = D / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, hh = lane >> 5;
+  __bf16* own = w < 2 ? tileA : tileB;
+  const int row = 32 * (w & 1) + (lane & 31);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * db + 8 * r4 + 4 * hh;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[db][4 * r4 + 0] * scale, acc[db][4 * r4 + 1] * scale);
+      pk[1] = pack_bf16x2(acc[db][4 * r4 + 2] * scale, acc[db][4 * r4 + 3] * scale);
+      *(u32x2*)(own + G::at(row, d0)) = pk;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const __bf16* src = half == 0 ? tileA : tileB;
+#pragma unroll
+    for (int u = 0; u < R::NU; ++u) {
+      const int r = R::row_of(tid, u);
+      __bf16* d = row_dst(kKTile * half + r);
+      const u32x4 v = *(const u32x4*)(src + (w * 1024 + u * NT * 16) / 2 + lane * 8);
+      if (d) *(u32x4*)(d + uoff[u] / 2 - (size_t)r * D) = v;
+    }
+  }
+}
+
 // Buffer resource over `bytes` bytes from `base` (raw, no stride).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
