@@ -39,7 +39,8 @@ constexpr float kLazy = 8.f;
 #define SEPATTN_FWD_OCC 4  // waves per SIMD the bf16 d=64 register budget targets (128 VGPRs, no spills)
 #endif
 #ifndef SEPATTN_FWD_QLDS
-#define SEPATTN_FWD_QLDS 1  // the query tile comes in through LDS (coalesced rows)
+#define SEPATTN_FWD_QLDS 128  // smallest head size whose Q tile and O rows go through LDS (coalesced rows):
+                              // at d=64 it measured no faster and its extra registers spill outside the loop
 #endif
 #ifndef SEPATTN_FWD_OCC128
 #define SEPATTN_FWD_OCC128 2  // d=128: two workgroups fill the LDS (64 KB each)
@@ -176,8 +177,8 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   fetch_anchor(min(1, n_tiles - 1));
 
   frag qf[NQF];
-#if SEPATTN_FWD_QLDS
-  if constexpr (EPL == 8) {
+#if SEPATTN_FWD_QLDS > 0
+  if constexpr (EPL == 8 && D >= SEPATTN_FWD_QLDS) {
     // The query tile comes in through the second pair of tile buffers (free
     // until tile 1 is issued) as two 64-row tiles, with the same coalesced
     // row loads as K and V, and each wave reads its 32 rows' fragments back;
@@ -329,8 +330,8 @@ __global__ void __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? (D == 64 ? SEPAT
   // normalise and store
   const float l_tot = pair_sum(l);
   const float inv = 1.f / l_tot;
-#if SEPATTN_FWD_QLDS
-  if constexpr (EPL == 8) {
+#if SEPATTN_FWD_QLDS > 0
+  if constexpr (EPL == 8 && D >= SEPATTN_FWD_QLDS) {
     // O goes out as whole rows: each wave puts its 32 rows into the first
     // pair of tile buffers (row-major, swizzled like every tile), then every
     // thread stores the 16-byte chunks a tile load would have brought in
