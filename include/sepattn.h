@@ -105,7 +105,10 @@ const char* sepattn_strerror(int status);
  *                                 [3] kt_end = q1 / 64
  *                                 [4] n_kept = ceil(n_anchor/64) + kt_end - kt_begin + 1
  *                                 [5] rows = q1 - q0 + 1
- *                                 [6] q0    [7] 0
+ *                                 [6] q0
+ *                                 [7] separators (at positions >= a) of the
+ *                                     tile's two 64-position blocks: first
+ *                                     block in bits 0..15, second in 16..31
  *   tile_class   [B, QT, KT] uint8 over the 128 x 64 grid of the S x S mask:
  *                                 0 no visible entry, 2 all visible, 1 otherwise
  * with QT = ceil(S/128), KT = ceil(S/64).  The visible keys of row i of tile
@@ -137,7 +140,11 @@ int sepattn_index_bind(void* buf, size_t bytes, int B, int S, sepattn_index* idx
  * (a >= 0) and window `n` (n >= 1).  idx must have been bound for the same
  * B and S; idx->a and idx->n are set, idx->n to min(n, S) (every n >= S
  * gives the same mask; sepattn_fwd and sepattn_bwd apply the same bound to
- * an idx->n set by hand).  Every output field is written. */
+ * an idx->n set by hand).  Every output field is written.  One launch, two
+ * from S >= 8192 on (a first one counts every tile's separators once, so
+ * the work below each query tile reads counts instead of tokens); the
+ * environment variable SEPATTN_INDEX_TWO_PASS_S, read at each call, moves
+ * that length (0: never).  Both give the same output. */
 int sepattn_build_index(const int32_t* token_ids, int B, int S, const int32_t* sep_ids, int n_sep,
                         int a, int n, sepattn_index* idx, void* stream);
 

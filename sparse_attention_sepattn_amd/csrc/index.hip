@@ -22,6 +22,14 @@
 //     row from the block's 64-bit separator mask;
 //   * flags, prefix counts and anchor-list entries of its own 128 positions;
 //   * (last query tile) the totals and the -1 padding of the anchor list.
+// The scan below a tile makes the whole launch O(S^2 / 8192) token reads
+// (tile_class itself has S^2 / 8192 entries).  For long sequences
+// (S >= SEPATTN_INDEX_TWO_PASS_S) a first launch counts the separators of
+// every 128-position tile once (qtile field 7, two 16-bit counts per tile)
+// and the second reads those counts instead of the tokens below its tile:
+// 1/64 of the bytes, no id comparisons.
+#include <stdlib.h>
+
 #include "internal.hpp"
 
 namespace sepattn {
@@ -31,6 +39,9 @@ namespace sepattn {
 #endif
 constexpr int kIdxThreads = SEPATTN_INDEX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / kWave;
+#ifndef SEPATTN_INDEX_TWO_PASS_S
+#define SEPATTN_INDEX_TWO_PASS_S 8192  // sequence length from which the separator counts come from a first launch
+#endif
 #ifndef SEPATTN_INDEX_BATCH
 #define SEPATTN_INDEX_BATCH 4
 #endif
@@ -55,8 +66,27 @@ __device__ __forceinline__ bool candidate(int32_t t, int j, const SepSet& sep, i
   return interval > 0 ? j % interval == interval - 1 : is_separator(sep, t);
 }
 
+// Separators (from position a on) of the two 64-position blocks of query
+// tile qi, packed into qtile field 7: low 16 bits the first block, high 16
+// bits the second.  One wave per (query tile, sequence).
+__global__ void __launch_bounds__(kWave)
+index_counts_kernel(const int32_t* __restrict__ tok, int S, int a, SepSet sep, int interval,
+                    int32_t* __restrict__ qtile) {
+  const int QT = gridDim.x;
+  const int qi = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int32_t* tk = tok ? tok + (size_t)b * S : nullptr;  // null with an interval
+  const int j0 = qi * kQTile + lane, j1 = j0 + kKTile;
+  const int32_t t0 = tk ? tk[min(j0, S - 1)] : 0, t1 = tk ? tk[min(j1, S - 1)] : 0;
+  const uint64_t m0 = __ballot(j0 < S && j0 >= a && candidate(t0, j0, sep, interval));
+  const uint64_t m1 = __ballot(j1 < S && j1 >= a && candidate(t1, j1, sep, interval));
+  if (lane == 0) qtile[((size_t)b * QT + qi) * kQF + 7] = __popcll(m0) | (__popcll(m1) << 16);
+}
+
+// counts = 1: the block counts below the tile come from qtile field 7 (set
+// by index_counts_kernel) instead of a scan of the tokens.
 __global__ void __launch_bounds__(kIdxThreads)
-index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, int interval,
+index_kernel(int counts, const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, int interval,
              uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_prefix, int32_t* __restrict__ anchor_pos,
              int32_t* __restrict__ anchor_count, int32_t* __restrict__ qtile, uint8_t* __restrict__ tile_class) {
   const int QT = gridDim.x;
@@ -101,8 +131,37 @@ index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, i
 #pragma unroll
     for (int e = 0; e < kIdxBatch; ++e) tv[e] = tk[min((base + e) * kKTile + lane, S - 1)];
   };
-  if (tok_ids && w * kIdxBatch < nb) load_pass(w * kIdxBatch);
-  for (int base = w * kIdxBatch; base < nb; base += kPass) {
+  if (counts) {
+    // (1') the same sums from the per-block counts: blocks below q0 (all of
+    // them in the last tile) and below lo; the block holding lo is counted
+    // from its tokens (wave 0); far-left classes from the counts
+    const int32_t* f7 = qtile + (size_t)b * QT * kQF + 7;
+    const int kl = lo / kKTile;
+    int c_q0 = 0, c_lo = 0, c_all = 0;
+    for (int kj = (int)threadIdx.x; kj < nb; kj += kIdxThreads) {
+      const int32_t pk = f7[(size_t)(kj >> 1) * kQF];
+      const int cnt = (kj & 1) ? (pk >> 16) : (pk & 0xFFFF);
+      c_all += cnt;
+      c_q0 += kj * kKTile < q0 ? cnt : 0;
+      c_lo += kj < kl ? cnt : 0;
+      if (kj < k_far) {
+        const int c0 = kj * kKTile;
+        const int v = min(max(a - c0, 0), kKTile) + cnt;  // visible keys per row (full-width tile)
+        cls[kj] = v == 0 ? 0 : (v == kKTile ? 2 : 1);
+      }
+    }
+    s_q0 = wave_sum(c_q0);
+    s_lo = wave_sum(c_lo);
+    s_all = wave_sum(c_all);
+    if (w == 0 && kl < nb) {
+      const int c0 = kl * kKTile;
+      const int j = c0 + lane;
+      const int32_t t = tok_ids ? tk[min(j, S - 1)] : 0;
+      s_lo += __popcll(__ballot(j < S && j >= a && candidate(t, j, sep, interval)) & low_bits(lo - c0));
+    }
+  }
+  if (!counts && tok_ids && w * kIdxBatch < nb) load_pass(w * kIdxBatch);
+  for (int base = w * kIdxBatch; !counts && base < nb; base += kPass) {
     bool hit[kIdxBatch];
     if (tok_ids) {
 #pragma unroll
@@ -198,7 +257,6 @@ index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, i
     f[4] = (n_anchor + kKTile - 1) / kKTile + ke - kb + 1;
     f[5] = q1 - q0 + 1;
     f[6] = q0;
-    f[7] = 0;
   }
 
   // (4) flags, prefix counts and anchor entries of positions [q0, q1]: wave 0
@@ -212,6 +270,8 @@ index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, i
     const uint64_t raw1 = __ballot(j1 < S && candidate(t_s1, j1, sep, interval));
     const uint64_t cnt0 = raw0 & ~low_bits(a - q0);
     const uint64_t cnt1 = raw1 & ~low_bits(a - q0 - kKTile);
+    if (!counts && w == 0 && lane == 0)
+      qtile[((size_t)b * QT + qi) * kQF + 7] = __popcll(cnt0) | (__popcll(cnt1) << 16);
     const uint64_t raw = w ? raw1 : raw0;
     const uint64_t cm = w ? cnt1 : cnt0;
     const int j = w ? j1 : j0;
@@ -237,7 +297,17 @@ index_kernel(const int32_t* __restrict__ tok, int S, int a, int n, SepSet sep, i
 hipError_t launch_build_index(const int32_t* tok, int B, int S, const SepSet& sep, int interval, int a, int n,
                               const sepattn_index& idx, hipStream_t stream) {
   const int QT = (S + kQTile - 1) / kQTile;
-  hipLaunchKernelGGL(index_kernel, dim3(QT, B), dim3(kIdxThreads), 0, stream, tok, S, a, n, sep, interval,
+  // the length from which the counts come from a first launch; the
+  // environment variable of the same name overrides the built-in value
+  int two_pass = SEPATTN_INDEX_TWO_PASS_S;
+  if (const char* e = getenv("SEPATTN_INDEX_TWO_PASS_S")) two_pass = atoi(e);
+  const int counts = two_pass > 0 && S >= two_pass;
+  if (counts) {
+    hipLaunchKernelGGL(index_counts_kernel, dim3(QT, B), dim3(kWave), 0, stream, tok, S, a, sep, interval, idx.qtile);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(index_kernel, dim3(QT, B), dim3(kIdxThreads), 0, stream, counts, tok, S, a, n, sep, interval,
                      idx.is_sep, idx.sep_prefix, idx.anchor_pos, idx.anchor_count, idx.qtile, idx.tile_class);
   return hipGetLastError();
 }

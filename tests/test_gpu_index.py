@@ -1,6 +1,8 @@
 """GPU parity of the index builder: every field bit-exact against the
 oracle's direct-counting definition, on i.i.d. and bursty separator streams,
-ragged lengths and degenerate parameters."""
+ragged lengths and degenerate parameters -- in the one-launch form and in
+the two-launch form long sequences use (forced here at every length through
+SEPATTN_INDEX_TWO_PASS_S)."""
 
 import numpy as np
 import pytest
@@ -28,6 +30,12 @@ def _check(tok, sep, a, n):
         qt = idx.qtile[b].cpu().numpy()
         assert np.array_equal(qt[:, :6], ref["qtile"])
         assert np.array_equal(qt[:, 6], 128 * np.arange(qt.shape[0]))
+        # field 7: separators of each tile's two 64-position blocks (from the
+        # oracle's prefix counts, which start at position a)
+        sp = ref["sep_prefix"].astype(np.int64)
+        edge = np.minimum(np.arange(0, 2 * qt.shape[0] + 1) * 64, S)
+        blk = sp[edge[1:]] - sp[edge[:-1]]
+        assert np.array_equal(qt[:, 7].astype(np.int64), blk[0::2] | (blk[1::2] << 16))
         assert np.array_equal(idx.tile_class[b].cpu().numpy(), ref["tile_class"])
 
 
@@ -64,3 +72,41 @@ def test_index_full_size(name):
     if cfg["B"] > 2:
         tok = tok[:2].copy()
     _check(tok, sep, cfg["a"], cfg["n"])
+
+
+@pytest.fixture
+def two_pass(monkeypatch):
+    """The two-launch index at every length for the duration of a test."""
+    monkeypatch.setenv("SEPATTN_INDEX_TWO_PASS_S", "1")
+
+
+@pytest.mark.parametrize("S,a,n,p", [(1, 4, 64, 0.5), (5, 0, 1, 0.5), (129, 4, 64, 0.08), (300, 0, 1000, 0.2),
+                                     (1000, 4, 64, 1.0), (8193, 4, 256, 0.08), (700, 100, 64, 0.1),
+                                     (200, 300, 5, 0.2), (1500, 70, 130, 0.05), (777, 64, 63, 0.3),
+                                     (1025, 1, 1, 0.9), (300, 4, 2**31 - 1, 0.1), (500, 2**31 - 1, 5, 0.1)])
+def test_index_two_pass_small_and_ragged(two_pass, S, a, n, p):
+    require_gpu()
+    r = synth.rng(S + a + n + 1)
+    sep = synth.separator_ids(r, 5000)
+    tok = synth.token_ids_iid(r, (3, S), 5000, sep, p)
+    _check(tok, sep, a, n)
+
+
+def test_index_two_pass_long_context(two_pass):
+    """The 32k-token bursty stream through the two-launch form."""
+    require_gpu()
+    cfg = synth.CONFIGS["long_context_32k"]
+    r = synth.rng(cfg["seed"])
+    sep = synth.separator_ids(r, cfg["vocab"])
+    tok = synth.token_ids_bursty(r, cfg["B"], cfg["S"], cfg["vocab"], sep)
+    _check(tok, sep, cfg["a"], cfg["n"])
+
+
+def test_index_past_two_pass_length():
+    """A 70000-token bursty stream: past the length from which the index takes
+    two launches by default (no override)."""
+    require_gpu()
+    r = synth.rng(70000)
+    sep = synth.separator_ids(r, 32000)
+    tok = synth.token_ids_bursty(r, 1, 70000, 32000, sep)
+    _check(tok, sep, 4, 256)

@@ -15,12 +15,17 @@ from tests.gpu_util import dev_tensor, host_f64, require_gpu, say
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
 @pytest.mark.parametrize("B,S,m,a,n", [(2, 1000, 12, 4, 64), (1, 4097, 1, 0, 5), (3, 333, 400, 2, 30),
                                        (1, 9000, 7, 4, 256), (1, 1, 3, 4, 64), (2, 129, 64, 0, 1)])
-def test_interval_index_bit_exact(B, S, m, a, n):
+def test_interval_index_bit_exact(B, S, m, a, n, two_pass, monkeypatch):
+    """Both forms of the index (one launch; two, with the per-tile separator
+    counts first, which long sequences use) at every shape."""
     require_gpu()
     import sparse_attention_sepattn_amd as sa
-    say(f"interval index B={B} S={S} m={m} a={a} n={n}")
+    if two_pass:
+        monkeypatch.setenv("SEPATTN_INDEX_TWO_PASS_S", "1")
+    say(f"interval index B={B} S={S} m={m} a={a} n={n} two_pass={two_pass}")
     idx = sa.build_index_interval(B, S, m, a, n)
     torch.cuda.synchronize()
     ref = sepmask.build_index_from_flags(sepmask.interval_flags(S, m), a, n)
