@@ -141,7 +141,7 @@ int sepattn_index_bind(void* buf, size_t bytes, int B, int S, sepattn_index* idx
  * B and S; idx->a and idx->n are set, idx->n to min(n, S) (every n >= S
  * gives the same mask; sepattn_fwd and sepattn_bwd apply the same bound to
  * an idx->n set by hand).  Every output field is written.  One launch, two
- * from S >= 8192 on (a first one counts every tile's separators once, so
+ * from S >= 16384 on (a first one counts every tile's separators once, so
  * the work below each query tile reads counts instead of tokens); the
  * environment variable SEPATTN_INDEX_TWO_PASS_S, read at each call, moves
  * that length (0: never).  Both give the same output. */

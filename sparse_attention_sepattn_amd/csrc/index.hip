@@ -40,7 +40,7 @@ namespace sepattn {
 constexpr int kIdxThreads = SEPATTN_INDEX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / kWave;
 #ifndef SEPATTN_INDEX_TWO_PASS_S
-#define SEPATTN_INDEX_TWO_PASS_S 8192  // sequence length from which the separator counts come from a first launch
+#define SEPATTN_INDEX_TWO_PASS_S 16384  // sequence length from which the separator counts come from a first launch
 #endif
 #ifndef SEPATTN_INDEX_BATCH
 #define SEPATTN_INDEX_BATCH 4
