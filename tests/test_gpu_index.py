@@ -110,3 +110,41 @@ def test_index_past_two_pass_length():
     sep = synth.separator_ids(r, 32000)
     tok = synth.token_ids_bursty(r, 1, 70000, 32000, sep)
     _check(tok, sep, 4, 256)
+
+
+def test_index_forms_agree_at_256k(monkeypatch):
+    """262144 tokens, 2 sequences with bursty separators: the one-launch and
+    the two-launch forms give the same index bit for bit, and every field of
+    the query tiles inside a 16384-token prefix equals the oracle's index of
+    that prefix (those fields depend on the prefix alone; the classes of key
+    tiles past it are 0)."""
+    require_gpu()
+    import sparse_attention_sepattn_amd as sa
+    B, S, P, a, n = 2, 262144, 16384, 4, 256
+    r = synth.rng(S)
+    sep = synth.separator_ids(r, 32000)
+    tok = synth.token_ids_bursty(r, B, S, 32000, sep)
+    tok_d = torch.from_numpy(tok).cuda()
+    got = []
+    for form in ("0", "1"):
+        monkeypatch.setenv("SEPATTN_INDEX_TWO_PASS_S", form)
+        say(f"index B={B} S={S} two_pass_from={form}")
+        idx = sa.build_index(tok_d, sep, a, n)
+        torch.cuda.synchronize()
+        got.append({k: getattr(idx, k).cpu().numpy() for k in
+                    ("is_sep", "sep_prefix", "anchor_pos", "anchor_count", "qtile", "tile_class")})
+    for k in got[0]:
+        assert np.array_equal(got[0][k], got[1][k]), k
+    g = got[1]
+    for b in range(B):
+        ref = sepmask.build_index(tok[b, :P], sep, a, n)
+        assert np.array_equal(g["is_sep"][b, :P], ref["is_sep"])
+        assert np.array_equal(g["sep_prefix"][b, :P + 1], ref["sep_prefix"])
+        m = ref["anchor_count"]
+        assert np.array_equal(g["anchor_pos"][b, :m], ref["anchor_pos"][:m])
+        assert g["anchor_count"][b] == min(a, S) + g["sep_prefix"][b, S]
+        qt = P // 128
+        assert np.array_equal(g["qtile"][b, :qt, :6], ref["qtile"])
+        kt = P // 64
+        assert np.array_equal(g["tile_class"][b, :qt, :kt], ref["tile_class"])
+        assert not g["tile_class"][b, :qt, kt:].any()
