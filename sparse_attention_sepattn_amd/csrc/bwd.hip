@@ -33,6 +33,8 @@
 // dQ^T = K^T dS^T.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "internal.hpp"
 #include "tile.hpp"
 
@@ -59,6 +61,9 @@ constexpr int bwd_occupancy() {
 // MI355X (8x12 heads of 2048 at d=64; 8 kv heads of 8192 and 32768 at
 // d=128, where the anchor columns carry most of the backward's work and the
 // time is not monotonic in the chunk count).
+#ifndef SEPATTN_ANCHOR_MAX_TILES
+#define SEPATTN_ANCHOR_MAX_TILES 40  // longest anchor chunk, in query tiles
+#endif
 #ifndef SEPATTN_ANCHOR_ITEMS64
 #define SEPATTN_ANCHOR_ITEMS64 256
 #endif
@@ -131,9 +136,17 @@ static void anchor_split(int B, int Hkv, int S, int QT, int d, int* nchunk, int*
   const long target = d <= 64 ? SEPATTN_ANCHOR_ITEMS64 : SEPATTN_ANCHOR_ITEMS128;
   long n = (target + (long)B * Hkv * units_guess - 1) / ((long)B * Hkv * units_guess);
   if (n < 1) n = 1;
-  if (n > 16) n = 16;
+  // once the anchor columns are split, chunks of at most
+  // SEPATTN_ANCHOR_MAX_TILES query tiles bound the longest anchor item
+  if (n > 1) n = std::max(n, (long)(QT + SEPATTN_ANCHOR_MAX_TILES - 1) / SEPATTN_ANCHOR_MAX_TILES);
+  if (n > 16) n = 16;  // the partial slots grow with the chunk count
   if (n > QT) n = QT;
-  const int ct = (int)((QT + n - 1) / n);
+  int ct = (int)((QT + n - 1) / n);
+  // with several chunks, never a power-of-two number of tiles: the items of
+  // different chunks that run side by side would then read rows a
+  // power-of-two stride apart (measured at 32k tokens: chunks of 32, 64 and
+  // 128 tiles 4.6-5.2 ms for the main kernel, of 26-86 other sizes 3.0-3.4 ms)
+  if (ct < QT && ct > 1 && (ct & (ct - 1)) == 0) ct = (QT + ct) / (ct + 1) <= 16 ? ct + 1 : ct - 1;
   *chunk_tiles = ct;
   *nchunk = (QT + ct - 1) / ct;
 }
