@@ -145,8 +145,9 @@ static void anchor_split(int B, int Hkv, int S, int QT, int d, int* nchunk, int*
   // with several chunks, never a power-of-two number of tiles: the items of
   // different chunks that run side by side would then read rows a
   // power-of-two stride apart (measured at 32k tokens: chunks of 32, 64 and
-  // 128 tiles 4.6-5.2 ms for the main kernel, of 26-86 other sizes 3.0-3.4 ms)
-  if (ct < QT && ct > 1 && (ct & (ct - 1)) == 0) ct = (QT + ct) / (ct + 1) <= 16 ? ct + 1 : ct - 1;
+  // 128 tiles 4.6-5.2 ms for the main kernel, of 26-86 other sizes
+  // 3.0-3.4 ms).  One tile more never makes more chunks.
+  if (ct < QT && ct > 1 && (ct & (ct - 1)) == 0) ct += 1;
   *chunk_tiles = ct;
   *nchunk = (QT + ct - 1) / ct;
 }
