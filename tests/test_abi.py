@@ -203,3 +203,37 @@ def test_binding_refuses_host_tensors():
         sa.fwd(q, k, k, None)
     with pytest.raises(TypeError, match="CUDA"):
         sa.bwd(q, k, k, q, torch.zeros((1, 2, 64)), q, None)
+
+
+def _anchor_chunks(B, Hq, Hkv, S, d):
+    """Anchor chunks of a bf16 backward, read off its workspace size: the
+    per-row (LSE, D) block plus, with several chunks, one fp32 dK and one dV
+    partial slot of [B, Hkv, S, d] per chunk."""
+    L = sa.load_library()
+    a256 = lambda x: (x + 255) // 256 * 256
+    ws = L.sepattn_bwd_workspace(B, Hq, Hkv, S, d, 1)
+    rest = ws - a256(B * Hq * ((S + 63) // 64) * 128 * 4)
+    slot = B * Hkv * S * d * 4
+    assert rest % (2 * slot) == 0, (ws, rest, slot)
+    return max(1, rest // (2 * slot))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,d,chunks", [
+    (8, 12, 12, 2048, 64, 1),     # Pythia-shaped: no split
+    (1, 32, 8, 8192, 128, 10),    # Llama-shaped 8k: 10 chunks of 7 query tiles
+    (1, 32, 8, 32768, 128, 7),    # 32k tokens: 3 by the item target, 7 once chunks stop at 40 tiles
+    (1, 12, 12, 12288, 64, 3),    # 2 by the target, 3 by the 40-tile bound (32 tiles, then 33)
+    (1, 2, 1, 2304, 128, 6),      # 9 by the target: 2 tiles (a power of two), then 3
+])
+def test_anchor_chunk_split(B, Hq, Hkv, S, d, chunks):
+    """The backward's anchor chunking: the item target, chunks of at most 40
+    query tiles once the anchor rows are split, never a power-of-two number
+    of tiles per chunk with several chunks, at most 16 chunks (host logic;
+    the GPU tests run these splits against the oracle)."""
+    assert _anchor_chunks(B, Hq, Hkv, S, d) == chunks
+
+
+def test_anchor_chunks_never_more_than_16():
+    for S in (4096, 16384, 65536, 131072, 262144):
+        for B, Hkv in ((1, 1), (1, 8), (4, 8)):
+            assert 1 <= _anchor_chunks(B, Hkv, Hkv, S, 128) <= 16

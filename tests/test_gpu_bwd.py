@@ -243,3 +243,44 @@ def test_autograd_function_matches_direct_calls():
     assert torch.equal(oa.detach(), o)
     for name, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), ref):
         assert torch.equal(got, want), name
+
+
+def test_bwd_split_adjusted_to_three_tiles():
+    """2304 tokens, one kv head: the item target asks for chunks of 2 query
+    tiles, a power of two, so the split takes 3 (6 chunks); every gradient
+    against the oracle."""
+    require_gpu()
+    inp = _inputs(2304, 1, 2, 1, 128, "bf16", 4, 256, 0.08, seed=2304)
+    got = _gpu_grads(inp)
+    c = inp["cfg"]
+    ref = attention.attention_backward(inp["qf"], inp["kf"], inp["vf"], inp["dof"], inp["tok"], inp["sep"],
+                                       c["a"], c["n"], scale=inp["scale"])
+    _check(got, ref, "bf16", "S=2304 split")
+
+
+def test_bwd_split_bounded_at_40_tiles():
+    """12288 tokens, 12 heads, d=64: the item target gives 2 chunks of 48
+    query tiles, the 40-tile bound 3 of 32, the power-of-two rule 33; dQ on
+    sampled rows, dK/dV on every anchor of the first 2048 positions and
+    sampled keys elsewhere, for the first and the last head."""
+    require_gpu()
+    inp = _inputs(12288, 1, 12, 12, 64, "bf16", 4, 64, 0.08, seed=12288)
+    c = inp["cfg"]
+    S = c["S"]
+    dq, dk, dv = _gpu_grads(inp)
+    sepf = sepmask.separator_flags(inp["tok"][0], inp["sep"])
+    rows = np.unique(np.concatenate([np.arange(0, S, 211), np.arange(S - 40, S)]))
+    early = np.concatenate([np.arange(0, c["a"]), np.nonzero(sepf[:2048])[0]])
+    cols = np.unique(np.concatenate([early, np.arange(0, S, 401)]))
+    for h in (0, 11):
+        ref = attention.grad_q_rows(inp["qf"][0, h], inp["kf"][0, h], inp["vf"][0, h], inp["dof"][0, h],
+                                    sepf, c["a"], c["n"], inp["scale"], rows)
+        rmax, rfro = _rel(dq[0, h, rows], ref)
+        say(f"  12k dq head {h}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+        assert rmax <= 3e-2 and rfro <= 1e-2
+        rk, rv = attention.grad_kv_cols([inp["qf"][0, h]], inp["kf"][0, h], inp["vf"][0, h], [inp["dof"][0, h]],
+                                        sepf, c["a"], c["n"], inp["scale"], cols)
+        for name, got, ref in (("dk", dk[0, h, cols], rk), ("dv", dv[0, h, cols], rv)):
+            rmax, rfro = _rel(got, ref)
+            say(f"  12k {name} head {h}: max-rel={rmax:.3g} fro-rel={rfro:.3g}")
+            assert rmax <= 3e-2 and rfro <= 1e-2
