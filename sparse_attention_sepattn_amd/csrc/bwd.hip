@@ -68,7 +68,7 @@ constexpr int bwd_occupancy() {
 #define SEPATTN_ANCHOR_ITEMS64 256
 #endif
 #ifndef SEPATTN_ANCHOR_ITEMS128
-#define SEPATTN_ANCHOR_ITEMS128 768
+#define SEPATTN_ANCHOR_ITEMS128 1024
 #endif
 // Waves per SIMD of the dQ kernel, and whether it uses the lean form (the
 // 32-key halves one after the other, K/V operands read in groups of 4, D
@@ -141,13 +141,7 @@ static void anchor_split(int B, int Hkv, int S, int QT, int d, int* nchunk, int*
   if (n > 1) n = std::max(n, (long)(QT + SEPATTN_ANCHOR_MAX_TILES - 1) / SEPATTN_ANCHOR_MAX_TILES);
   if (n > 16) n = 16;  // the partial slots grow with the chunk count
   if (n > QT) n = QT;
-  int ct = (int)((QT + n - 1) / n);
-  // with several chunks, never a power-of-two number of tiles: the items of
-  // different chunks that run side by side would then read rows a
-  // power-of-two stride apart (measured at 32k tokens: chunks of 32, 64 and
-  // 128 tiles 4.6-5.2 ms for the main kernel, of 26-86 other sizes
-  // 3.0-3.4 ms).  One tile more never makes more chunks.
-  if (ct < QT && ct > 1 && (ct & (ct - 1)) == 0) ct += 1;
+  const int ct = (int)((QT + n - 1) / n);
   *chunk_tiles = ct;
   *nchunk = (QT + ct - 1) / ct;
 }
@@ -778,12 +772,17 @@ __global__ void __launch_bounds__(kBwdThreads, (bwd_occupancy<T, D>())) bwd_main
   if (x < p.n_anchor_items) {
     // lane-major so the first anchor units come first; a lane's items are
     // padded to a multiple of the 8 XCDs (anchor_stride), so that every lane
-    // of one (sequence, kv head, chunk) runs on the same XCD
+    // of one (sequence, kv head, chunk) runs on the same XCD.  Chunk-major
+    // within a lane: the XCD of a group is (chunk * B*Hkv + bg) mod 8, so
+    // with B*Hkv a multiple of 8 every XCD gets all chunks of its (sequence,
+    // kv head)s; numbered bg-major instead, (bg * nchunk + chunk) mod 8, an
+    // even chunk count gives each XCD only some chunk indices, and the later
+    // chunks hold far more anchor work
     const int lane0 = x / p.anchor_stride;
     const int r = x - lane0 * p.anchor_stride;
     if (r >= BG * p.nchunk) return;
-    const int bg = r / p.nchunk;
-    const int chunk = r - bg * p.nchunk;
+    const int chunk = r / BG;
+    const int bg = r - chunk * BG;
     for (int unit = lane0; unit < p.units; unit += p.anchor_lanes) {
       if (!dkdv_item<T, D, true>(p, bg / p.Hkv, bg % p.Hkv, unit, chunk, sm)) break;
       __syncthreads();  // the next unit refills the tile buffers

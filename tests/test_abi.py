@@ -220,16 +220,15 @@ def _anchor_chunks(B, Hq, Hkv, S, d):
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,d,chunks", [
     (8, 12, 12, 2048, 64, 1),     # Pythia-shaped: no split
-    (1, 32, 8, 8192, 128, 10),    # Llama-shaped 8k: 10 chunks of 7 query tiles
-    (1, 32, 8, 32768, 128, 7),    # 32k tokens: 3 by the item target, 7 once chunks stop at 40 tiles
-    (1, 12, 12, 12288, 64, 3),    # 2 by the target, 3 by the 40-tile bound (32 tiles, then 33)
-    (1, 2, 1, 2304, 128, 6),      # 9 by the target: 2 tiles (a power of two), then 3
+    (1, 32, 8, 8192, 128, 13),    # Llama-shaped 8k: 13 chunks of 5 query tiles
+    (1, 32, 8, 32768, 128, 7),    # 32k tokens: 4 by the item target, 7 once chunks stop at 40 tiles
+    (1, 12, 12, 12288, 64, 3),    # 2 by the target, 3 by the 40-tile bound
+    (1, 2, 1, 2304, 128, 9),      # 256 by the target: 16 at most, so chunks of 2 tiles
 ])
 def test_anchor_chunk_split(B, Hq, Hkv, S, d, chunks):
     """The backward's anchor chunking: the item target, chunks of at most 40
-    query tiles once the anchor rows are split, never a power-of-two number
-    of tiles per chunk with several chunks, at most 16 chunks (host logic;
-    the GPU tests run these splits against the oracle)."""
+    query tiles once the anchor rows are split, at most 16 chunks (host
+    logic; the GPU tests run these splits against the oracle)."""
     assert _anchor_chunks(B, Hq, Hkv, S, d) == chunks
 
 

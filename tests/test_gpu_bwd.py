@@ -245,10 +245,10 @@ def test_autograd_function_matches_direct_calls():
         assert torch.equal(got, want), name
 
 
-def test_bwd_split_adjusted_to_three_tiles():
-    """2304 tokens, one kv head: the item target asks for chunks of 2 query
-    tiles, a power of two, so the split takes 3 (6 chunks); every gradient
-    against the oracle."""
+def test_bwd_many_short_anchor_chunks():
+    """2304 tokens, one kv head: the split's upper bound of 16 chunks gives 9
+    chunks of 2 query tiles, so most anchors sum 9 partial slots; every
+    gradient against the oracle."""
     require_gpu()
     inp = _inputs(2304, 1, 2, 1, 128, "bf16", 4, 256, 0.08, seed=2304)
     got = _gpu_grads(inp)
@@ -260,9 +260,9 @@ def test_bwd_split_adjusted_to_three_tiles():
 
 def test_bwd_split_bounded_at_40_tiles():
     """12288 tokens, 12 heads, d=64: the item target gives 2 chunks of 48
-    query tiles, the 40-tile bound 3 of 32, the power-of-two rule 33; dQ on
-    sampled rows, dK/dV on every anchor of the first 2048 positions and
-    sampled keys elsewhere, for the first and the last head."""
+    query tiles, the 40-tile bound 3 of 32; dQ on sampled rows, dK/dV on
+    every anchor of the first 2048 positions and sampled keys elsewhere, for
+    the first and the last head."""
     require_gpu()
     inp = _inputs(12288, 1, 12, 12, 64, "bf16", 4, 64, 0.08, seed=12288)
     c = inp["cfg"]
